@@ -1,0 +1,244 @@
+"""fp64 CPU oracle for Multi-head Latent Attention (MLA) decode over a latent KV cache.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library
+never calls it, and the two share no code: no kernels, headers, helpers,
+tables or constants.  Inputs reach both sides as plain arrays.
+
+It computes the plain definition, slowly and visibly, in float64:
+  * the cache row of a token is the joint latent c = W^DKV h followed by the
+    decoupled key k^R = RoPE_pos(W^KR h), rounded once to the storage type;
+  * every head's key and value are decompressed from the latent
+    (k^C = W^UK_i c, v = W^UV_i c): no matrix absorption;
+  * the rotary key k^R is concatenated to each head's key, the rotary query
+    q^R to each head's query, and standard softmax attention runs per head.
+Matrix absorption is written separately (``decode_absorbed``) only so that a
+test can check the two agree.
+
+Pages (title, section) that fix what is computed:
+  [V2]  "DeepSeek-V2: Multi-Head Latent Attention (MLA) 原理与工程实现"
+        §1.1 (MHA and its per-token cache), §1.2 (MQA/GQA cache),
+        §2.1 (joint low-rank compression, up-projections), §2.2 (absorption),
+        §3.2 (decoupled RoPE: multi-head q^R, one shared k^R, concatenation),
+        §3.3 (cache = d_c + d_h^R per token per layer).
+  [QD]  "【深度学习】DeepSeek焦点架构-MLA：分析低秩联合压缩优化KV缓存、提升推理 ..."
+        02 (2)-(5) (joint K/V compression, decoupled RoPE, per-head concat),
+        04 (cache comparison).
+  [R1]  "R1的 MLA是如何节约 KV cache的?" §2.2 (weight fusion identity).
+  [KV]  "kv-cache 的优化学习" (the MHA demo: softmax(QK^T/sqrt(D))V per head).
+
+Readings where the pages are silent (each listed in the design notes):
+  * RoPE pairs are interleaved, (x_{2i}, x_{2i+1}) rotated by pos*theta_i with
+    theta_i = base^(-2i/d); positions are 0-based.
+  * k^R is cached after rotation; q^R handed to decode is already rotated.
+  * query s of a group of Sq attends cached tokens 0 .. L-Sq+s (itself included).
+  * cache rows are rounded to the storage type (bf16: nearest-even).
+  * a query that sees no token returns zeros and lse = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "round_to_storage", "rope", "cache_rows", "write_rows", "q_project", "gather_rows",
+    "decode", "decode_absorbed", "latent_elements_per_token", "mha_elements_per_token",
+    "mqa_elements_per_token", "gqa_elements_per_token",
+]
+
+
+# ---------------------------------------------------------------------------
+# storage rounding (part of what a bf16 / fp32 cache *is*)
+# ---------------------------------------------------------------------------
+def _round_significand(x: np.ndarray, sig_bits: int, min_exp: int, max_exp: int) -> np.ndarray:
+    """Round float64 values to a binary format with ``sig_bits`` significant bits
+    (implicit bit included), round-to-nearest-even, gradual underflow below
+    2^min_exp, overflow to +-inf above the largest finite value."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                        # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e - sig_bits, min_exp - sig_bits + 1).astype(np.float64)
+    quantum = np.ldexp(1.0, q.astype(np.int64))
+    r = np.rint(x / quantum) * quantum        # rint: ties to even
+    largest = (2.0 - 2.0 ** (1 - sig_bits)) * 2.0 ** max_exp
+    return np.where(np.abs(r) > largest, np.copysign(np.inf, x), r)
+
+
+def round_to_storage(x: np.ndarray, storage: str) -> np.ndarray:
+    """Values of ``x`` after storing them as ``storage`` ('bf16', 'f32' or 'f64')."""
+    if storage == "bf16":
+        return _round_significand(x, 8, -126, 127)
+    if storage == "f32":
+        return _round_significand(x, 24, -126, 127)
+    if storage == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(storage)
+
+
+# ---------------------------------------------------------------------------
+# decoupled RoPE  ([V2] §3.2; RoPE itself is RoFormer's rotation)
+# ---------------------------------------------------------------------------
+def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotate consecutive pairs (x_{2i}, x_{2i+1}) by angle pos * base^(-2i/d).
+
+    ``x`` has the rotary dimension last; ``pos`` broadcasts against x[..., 0]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    i = np.arange(d // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * i / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    even, odd = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
+    out[..., 0::2] = even * c - odd * s
+    out[..., 1::2] = even * s + odd * c
+    return out
+
+
+# ---------------------------------------------------------------------------
+# append: what one token leaves in the cache  ([V2] §2.1, §3.2, §3.3; [QD] 02 (2), 04 (2))
+# ---------------------------------------------------------------------------
+def cache_rows(h, w_dkv, w_kr, positions, rope_base: float, storage: str) -> np.ndarray:
+    """Cache rows [c^KV ‖ k^R] for hidden states ``h`` [B, T, d].
+
+    c^KV = W^DKV h (W^DKV is d_c x d); k^R = RoPE_pos(W^KR h) (W^KR is d_R x d);
+    the concatenation is rounded once to ``storage``."""
+    h = np.asarray(h, dtype=np.float64)
+    c = h @ np.asarray(w_dkv, dtype=np.float64).T
+    kr = rope(h @ np.asarray(w_kr, dtype=np.float64).T, positions, rope_base)
+    return round_to_storage(np.concatenate([c, kr], axis=-1), storage)
+
+
+def write_rows(pool: np.ndarray, block_table, positions, rows, block_size: int) -> None:
+    """Paged write: the row of sequence b at position p goes to
+    pool[block_table[b, p // block_size], p % block_size]."""
+    positions = np.asarray(positions)
+    for b in range(positions.shape[0]):
+        for t in range(positions.shape[1]):
+            p = int(positions[b, t])
+            pool[int(block_table[b, p // block_size]), p % block_size, :] = rows[b, t]
+
+
+def gather_rows(pool, block_table, seq_len: int, block_size: int) -> np.ndarray:
+    """The L cached rows of one sequence, in logical order, as float64 [L, R]."""
+    j = np.arange(seq_len)
+    return np.asarray(pool[np.asarray(block_table)[j // block_size], j % block_size], dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# query path  ([V2] §1.1 W^Q applied to h, §3.2 q^R = RoPE(W^QR h) per head)
+# ---------------------------------------------------------------------------
+def q_project(h, w_q, w_qr, positions, n_heads: int, rope_base: float):
+    """q^C_i = W^Q_i h and q^R_i = RoPE_pos(W^QR_i h) for each head i.
+
+    ``h`` [B, S, d]; returns float64 q_nope [B, S, H, d_nope], q_rope [B, S, H, d_R]."""
+    h = np.asarray(h, dtype=np.float64)
+    B, S, _ = h.shape
+    qn = (h @ np.asarray(w_q, dtype=np.float64).T).reshape(B, S, n_heads, -1)
+    qr = (h @ np.asarray(w_qr, dtype=np.float64).T).reshape(B, S, n_heads, -1)
+    return qn, rope(qr, np.asarray(positions)[..., None], rope_base)
+
+
+# ---------------------------------------------------------------------------
+# decode, non-absorbed: the oracle proper
+# ---------------------------------------------------------------------------
+def _softmax_attend(z: np.ndarray, v: np.ndarray):
+    """Stable softmax over the last axis of the logits z [n], then weights @ v [n, d]."""
+    m = z.max()
+    e = np.exp(z - m)
+    den = e.sum()
+    return (e / den) @ v, m + math.log(den)
+
+
+def decode(q_nope, q_rope, w_uk, w_uv, pool, block_table, seq_lens, scale: float,
+           block_size: int, heads=None, batches=None):
+    """MLA decode by decompression.
+
+    For sequence b with L cached tokens (the Sq query tokens included) and head i:
+      K^C_j = W^UK_i c_j, V_j = W^UV_i c_j, with W^UK_i, W^UV_i the rows
+      i*d_h .. (i+1)*d_h - 1 of W^UK, W^UV  ([V2] §2.1);
+      k_j = [K^C_j ; k^R_j], q_s = [q^C_s ; q^R_s]  ([V2] §3.2);
+      z_j = scale * q_s . k_j for j <= L - Sq + s; o = softmax(z) V ([KV] demo_mha).
+    Returns float64 out [B, Sq, H, d_h] and lse [B, Sq, H] (natural log of the
+    sum of exp(z)); rows not in ``heads`` / ``batches`` are left NaN."""
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    B, Sq, H, dn = q_nope.shape
+    dc = w_uk.shape[1]
+    out = np.full((B, Sq, H, dn), np.nan)
+    lse = np.full((B, Sq, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seq_lens[b])
+        rows = gather_rows(pool, block_table[b], L, block_size) if L > 0 else np.zeros((0, w_uk.shape[1] + q_rope.shape[-1]))
+        c, kr = rows[:, :dc], rows[:, dc:]
+        for i in (range(H) if heads is None else heads):
+            wk = w_uk[i * dn:(i + 1) * dn]            # d_h x d_c
+            wv = w_uv[i * dn:(i + 1) * dn]
+            k = np.concatenate([c @ wk.T, kr], axis=1)  # L x (d_h + d_R)
+            v = c @ wv.T                                # L x d_h
+            for s in range(Sq):
+                n = L - Sq + s + 1
+                if n <= 0:
+                    out[b, s, i], lse[b, s, i] = 0.0, -np.inf
+                    continue
+                q = np.concatenate([q_nope[b, s, i], q_rope[b, s, i]])
+                out[b, s, i], lse[b, s, i] = _softmax_attend(scale * (k[:n] @ q), v[:n])
+    return out, lse
+
+
+def decode_absorbed(q_nope, q_rope, w_uk, w_uv, pool, block_table, seq_lens, scale: float,
+                    block_size: int, heads=None, batches=None):
+    """The same decode with W^UK absorbed into the query and W^UV applied after the
+    weighted sum ([V2] §2.2; [R1] §2.2): q~ = W^UK_i^T q^C,
+    z_j = scale * (q~ . c_j + q^R . k^R_j), o = W^UV_i (sum_j p_j c_j).
+    Exists only so a test can check that absorption is exact."""
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    B, Sq, H, dn = q_nope.shape
+    dc = w_uk.shape[1]
+    out = np.full((B, Sq, H, dn), np.nan)
+    lse = np.full((B, Sq, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seq_lens[b])
+        rows = gather_rows(pool, block_table[b], L, block_size)
+        c, kr = rows[:, :dc], rows[:, dc:]
+        for i in (range(H) if heads is None else heads):
+            wk = w_uk[i * dn:(i + 1) * dn]
+            wv = w_uv[i * dn:(i + 1) * dn]
+            for s in range(Sq):
+                n = L - Sq + s + 1
+                if n <= 0:
+                    out[b, s, i], lse[b, s, i] = 0.0, -np.inf
+                    continue
+                q_lat = wk.T @ q_nope[b, s, i]                  # d_c
+                z = scale * (c[:n] @ q_lat + kr[:n] @ q_rope[b, s, i])
+                o_lat, lse[b, s, i] = _softmax_attend(z, c[:n])  # latent weighted sum
+                out[b, s, i] = wv @ o_lat
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# cache accounting, elements per token per layer
+# ---------------------------------------------------------------------------
+def latent_elements_per_token(d_latent: int, d_rope: int) -> int:
+    """MLA caches c^KV and k^R: d_c + d_h^R elements ([V2] §3.3; [QD] 04 (2))."""
+    return d_latent + d_rope
+
+
+def mha_elements_per_token(n_heads: int, d_head: int) -> int:
+    """MHA caches every head's key and value: 2 n_h d_h elements ([V2] §1.1; [QD] 04 (1))."""
+    return 2 * n_heads * d_head
+
+
+def mqa_elements_per_token(d_head: int) -> int:
+    """One shared key/value head: 2 d_h elements ([V2] §1.2)."""
+    return 2 * d_head
+
+
+def gqa_elements_per_token(n_groups: int, d_head: int) -> int:
+    """n_g shared key/value heads: 2 n_g d_h elements ([V2] §1.2)."""
+    return 2 * n_groups * d_head

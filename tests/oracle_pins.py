@@ -1,0 +1,324 @@
+"""Pins for the fp64 oracle: checks against what the pages and plain mathematics fix.
+
+Each ``pin_*`` function takes the oracle module (so a test can hand in a copy
+with a planted mistake) and returns the worst error it saw; the pin passes when
+that error is below ``PIN_TOL``.  None of these re-types the oracle's own
+formula: each compares with a textbook special case written as explicit
+loops, a closed form, an invariant, exact rational arithmetic, or a library
+routine.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+PIN_TOL = 1e-10
+
+
+def _rng(seed):
+    return np.random.default_rng(1000 + seed)
+
+
+def _paged_case(rng, B, H, dn, dr, dc, lens, bs, Sq):
+    """Random fp64 decode inputs with a permuted block table."""
+    nblk = [(L + bs - 1) // bs for L in lens]
+    total = sum(nblk)
+    perm = rng.permutation(total)
+    bt = np.full((B, max(nblk)), -1, dtype=np.int64)
+    o = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    pool = rng.standard_normal((total, bs, dc + dr))
+    qn = rng.standard_normal((B, Sq, H, dn))
+    qr = rng.standard_normal((B, Sq, H, dr))
+    wuk = rng.standard_normal((H * dn, dc)) / math.sqrt(dc)
+    wuv = rng.standard_normal((H * dn, dc)) / math.sqrt(dc)
+    return qn, qr, wuk, wuv, pool, bt
+
+
+# ---------------------------------------------------------------- storage
+def pin_bf16_rounding(orc) -> float:
+    """bf16 rounding equals torch's float32 -> bfloat16 cast (nearest-even) on
+    float32-exact inputs, plus hand-worked ties."""
+    import torch
+    rng = _rng(1)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    lib = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    err = float(np.max(np.abs(orc.round_to_storage(x32.astype(np.float64), "bf16") - lib) / np.maximum(np.abs(lib), 1e-300)))
+    # ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1);
+    #       1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    ties = orc.round_to_storage(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)]), "bf16")
+    want = np.array([1.0, 1 + 2.0 ** -6, -1.0])
+    return max(err, float(np.max(np.abs(ties - want))))
+
+
+def pin_f32_rounding(orc) -> float:
+    """fp32 rounding equals numpy's float64 -> float32 cast, subnormals and overflow included."""
+    rng = _rng(2)
+    x = rng.standard_normal(20000) * np.exp(rng.uniform(-110, 90, 20000))
+    x = np.concatenate([x, [3.5e38, -3.5e38, 1e-45, 7e-46, 0.0]])
+    with np.errstate(over="ignore"):
+        lib = x.astype(np.float32).astype(np.float64)
+    mine = orc.round_to_storage(x, "f32")
+    same = (mine == lib) | (np.isinf(mine) & np.isinf(lib) & (np.sign(mine) == np.sign(lib)))
+    return 0.0 if bool(np.all(same)) else 1.0
+
+
+# ---------------------------------------------------------------- RoPE
+def pin_rope_rotation(orc) -> float:
+    """RoPE as RoFormer's complex form: pair (x_{2i}, x_{2i+1}) read as the complex
+    number x_{2i} + i x_{2i+1}, multiplied by exp(i p base^(-2i/d)).  Also: norm
+    kept, identity at p = 0, and the score depends only on m - n."""
+    rng = _rng(3)
+    d, base = 8, 10000.0
+    x = rng.standard_normal((5, d))
+    pos = np.array([0, 1, 17, 4095, 8191])
+    got = orc.rope(x, pos, base)
+    err = 0.0
+    for r in range(5):
+        for i in range(d // 2):
+            z = complex(x[r, 2 * i], x[r, 2 * i + 1]) * complex(math.cos(pos[r] * base ** (-2 * i / d)),
+                                                                  math.sin(pos[r] * base ** (-2 * i / d)))
+            err = max(err, abs(got[r, 2 * i] - z.real), abs(got[r, 2 * i + 1] - z.imag))
+    err = max(err, float(np.max(np.abs(np.linalg.norm(got, axis=1) - np.linalg.norm(x, axis=1)))))
+    err = max(err, float(np.max(np.abs(got[0] - x[0]))))
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n in [(5, 2), (103, 100), (9000, 8997)]:
+        a = orc.rope(q, np.array(m), base) @ orc.rope(k, np.array(n), base)
+        b = orc.rope(q, np.array(m - n), base) @ k
+        err = max(err, abs(a - b))
+    return err
+
+
+# ---------------------------------------------------------------- absorption
+def pin_absorption(orc) -> float:
+    """Decompress-then-attend equals the absorbed latent-space form (associativity)."""
+    rng = _rng(4)
+    B, H, dn, dr, dc, bs, Sq = 2, 4, 8, 4, 16, 16, 2
+    lens = [37, 16]
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, B, H, dn, dr, dc, lens, bs, Sq)
+    o1, l1 = orc.decode(qn, qr, wuk, wuv, pool, bt, lens, 0.3, bs)
+    o2, l2 = orc.decode_absorbed(qn, qr, wuk, wuv, pool, bt, lens, 0.3, bs)
+    return float(max(np.max(np.abs(o1 - o2)) / np.max(np.abs(o1)), np.max(np.abs(l1 - l2))))
+
+
+# ---------------------------------------------------------------- textbook MHA
+def _mha_loops(x, wq, wk, wv, H, D):
+    """softmax(q k^T / sqrt(D)) v per head for the last position, as explicit loops."""
+    L, d = x.shape
+    def proj(w, t, row):
+        return sum(w[row][c] * x[t][c] for c in range(d))
+    out = [[0.0] * D for _ in range(H)]
+    for hh in range(H):
+        q = [proj(wq, L - 1, hh * D + e) for e in range(D)]
+        z = []
+        for t in range(L):
+            k = [proj(wk, t, hh * D + e) for e in range(D)]
+            z.append(sum(q[e] * k[e] for e in range(D)) / math.sqrt(D))
+        mx = max(z)
+        w = [math.exp(zz - mx) for zz in z]
+        s = sum(w)
+        for t in range(L):
+            v = [proj(wv, t, hh * D + e) for e in range(D)]
+            for e in range(D):
+                out[hh][e] += w[t] / s * v[e]
+    return np.array(out)
+
+
+def pin_mha_special_case(orc) -> float:
+    """With d_c = 2 n_h d_h, W^DKV = [W_K; W_V], W^UK = [I 0], W^UV = [0 I] and zero
+    rotary weights, the whole MLA path (append, query projection, decode) is
+    plain MHA, checked against explicit loops."""
+    rng = _rng(5)
+    H, D, d, L, dr, bs = 2, 4, 6, 5, 2, 4
+    x = rng.standard_normal((L, d))
+    wq, wk, wv = (rng.standard_normal((H * D, d)) for _ in range(3))
+    dc = 2 * H * D
+    w_dkv = np.concatenate([wk, wv], axis=0)
+    eye = np.eye(H * D)
+    w_uk = np.concatenate([eye, np.zeros((H * D, H * D))], axis=1)
+    w_uv = np.concatenate([np.zeros((H * D, H * D)), eye], axis=1)
+    w_kr = np.zeros((dr, d))
+    w_qr = np.zeros((H * dr, d))
+    pos = np.arange(L)[None, :]
+    rows = orc.cache_rows(x[None], w_dkv, w_kr, pos, 10000.0, "f64")
+    nblk = (L + bs - 1) // bs
+    pool = np.full((nblk, bs, dc + dr), 7.0)
+    bt = np.arange(nblk)[None, :]
+    orc.write_rows(pool, bt, pos, rows, bs)
+    qn, qr = orc.q_project(x[None, L - 1:L], wq, w_qr, pos[:, L - 1:], H, 10000.0)
+    out, _ = orc.decode(qn, qr, w_uk, w_uv, pool, bt, [L], 1.0 / math.sqrt(D), bs)
+    ref = _mha_loops(x, wq, wk, wv, H, D)
+    return float(np.max(np.abs(out[0, 0] - ref)))
+
+
+# ---------------------------------------------------------------- MQA on the rotary key
+def pin_mqa_special_case(orc) -> float:
+    """With q^C = 0 and one W^UV shared by every head, every head attends the one
+    shared key k^R with one shared value: MQA, checked against explicit loops."""
+    rng = _rng(6)
+    H, dn, dr, dc, bs, L = 3, 4, 4, 6, 8, 11
+    qn, qr, wuk, _, pool, bt = _paged_case(rng, 1, H, dn, dr, dc, [L], bs, 1)
+    qn[:] = 0.0
+    w1 = rng.standard_normal((dn, dc))
+    wuv = np.concatenate([w1] * H, axis=0)
+    scale = 0.7
+    out, _ = orc.decode(qn, qr, wuk, wuv, pool, bt, [L], scale, bs)
+    err = 0.0
+    rows = [pool[bt[0, t // bs], t % bs] for t in range(L)]
+    for hh in range(H):
+        z = [scale * sum(qr[0, 0, hh, e] * rows[t][dc + e] for e in range(dr)) for t in range(L)]
+        mx = max(z)
+        w = [math.exp(v - mx) for v in z]
+        s = sum(w)
+        for e in range(dn):
+            ref = sum(w[t] / s * sum(w1[e][c] * rows[t][c] for c in range(dc)) for t in range(L))
+            err = max(err, abs(out[0, 0, hh, e] - ref))
+    return err
+
+
+# ---------------------------------------------------------------- closed forms / invariants
+def pin_softmax_normalised(orc) -> float:
+    """If every cached latent has c_0 = 1 and row 0 of each W^UV_i is e_0, output
+    element 0 is the sum of the attention weights: exactly 1."""
+    rng = _rng(7)
+    H, dn, dr, dc, bs = 3, 4, 2, 8, 8
+    lens = [1, 9, 30]
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, 3, H, dn, dr, dc, lens, bs, 1)
+    qn *= 5.0
+    pool[:, :, 0] = 1.0
+    for hh in range(H):
+        wuv[hh * dn] = 0.0
+        wuv[hh * dn, 0] = 1.0
+    out, _ = orc.decode(qn, qr, wuk, wuv, pool, bt, lens, 0.5, bs)
+    return float(np.max(np.abs(out[:, :, :, 0] - 1.0)))
+
+
+def pin_closed_forms(orc) -> float:
+    """One visible token: o = W^UV_i c_0.  Zero query: o = mean_j W^UV_i c_j and
+    lse = ln(n).  With Sq = 2 and L = 2 the first query sees only token 0."""
+    rng = _rng(8)
+    H, dn, dr, dc, bs = 2, 4, 2, 6, 4
+    err = 0.0
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, 1, H, dn, dr, dc, [1], bs, 1)
+    out, lse = orc.decode(qn, qr, wuk, wuv, pool, bt, [1], 0.9, bs)
+    c0 = pool[bt[0, 0], 0, :dc]
+    for hh in range(H):
+        err = max(err, float(np.max(np.abs(out[0, 0, hh] - wuv[hh * dn:(hh + 1) * dn] @ c0))))
+    L = 13
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, 1, H, dn, dr, dc, [L], bs, 1)
+    qn[:] = 0.0
+    qr[:] = 0.0
+    out, lse = orc.decode(qn, qr, wuk, wuv, pool, bt, [L], 0.9, bs)
+    cs = np.array([pool[bt[0, t // bs], t % bs, :dc] for t in range(L)])
+    for hh in range(H):
+        err = max(err, float(np.max(np.abs(out[0, 0, hh] - wuv[hh * dn:(hh + 1) * dn] @ cs.mean(0)))))
+        err = max(err, abs(lse[0, 0, hh] - math.log(L)))
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, 1, H, dn, dr, dc, [2], bs, 2)
+    out, _ = orc.decode(qn, qr, wuk, wuv, pool, bt, [2], 0.9, bs)
+    c0 = pool[bt[0, 0], 0, :dc]
+    for hh in range(H):
+        err = max(err, float(np.max(np.abs(out[0, 0, hh] - wuv[hh * dn:(hh + 1) * dn] @ c0))))
+    return err
+
+
+def pin_causal_group(orc) -> float:
+    """Query s of an Sq-group over L tokens equals a single query over the first
+    L - Sq + s + 1 tokens."""
+    rng = _rng(9)
+    H, dn, dr, dc, bs, L, Sq = 2, 4, 2, 6, 4, 10, 3
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, 1, H, dn, dr, dc, [L], bs, Sq)
+    out, lse = orc.decode(qn, qr, wuk, wuv, pool, bt, [L], 0.8, bs)
+    err = 0.0
+    for s in range(Sq):
+        o1, l1 = orc.decode(qn[:, s:s + 1], qr[:, s:s + 1], wuk, wuv, pool, bt, [L - Sq + s + 1], 0.8, bs)
+        err = max(err, float(np.max(np.abs(out[:, s] - o1[:, 0]))), float(np.max(np.abs(lse[:, s] - l1[:, 0]))))
+    return err
+
+
+def pin_paging(orc) -> float:
+    """A permuted block table over a permuted pool gives the same result as the
+    identity table over the contiguous pool."""
+    rng = _rng(10)
+    H, dn, dr, dc, bs = 2, 4, 2, 6, 4
+    lens = [9, 14]
+    qn, qr, wuk, wuv, pool, bt = _paged_case(rng, 2, H, dn, dr, dc, lens, bs, 1)
+    o1, _ = orc.decode(qn, qr, wuk, wuv, pool, bt, lens, 0.8, bs)
+    contiguous = np.zeros((2, 4, bs, dc + dr))
+    for b in range(2):
+        for i in range((lens[b] + bs - 1) // bs):
+            contiguous[b, i] = pool[bt[b, i]]
+    bt2 = np.arange(8).reshape(2, 4)
+    o2, _ = orc.decode(qn, qr, wuk, wuv, contiguous.reshape(8, bs, dc + dr), bt2, lens, 0.8, bs)
+    return float(np.max(np.abs(o1 - o2)))
+
+
+# ---------------------------------------------------------------- append
+def pin_append_exact(orc) -> float:
+    """On dyadic inputs the latent row c = W^DKV h is exact rational arithmetic;
+    the rotary part at position 0 is the unrotated W^KR h; rows land in the slot
+    the block table names and nowhere else."""
+    rng = _rng(11)
+    d, dc, dr, bs = 12, 6, 4, 4
+    h = rng.integers(-2, 3, size=(2, 3, d)).astype(np.float64)
+    w_dkv = rng.integers(-64, 65, size=(dc, d)) / 64.0
+    w_kr = rng.integers(-64, 65, size=(dr, d)) / 64.0
+    pos = np.array([[0, 5, 6], [0, 1, 9]])
+    import torch
+    rows = orc.cache_rows(h, w_dkv, w_kr, pos, 10000.0, "bf16")
+    err = 0.0
+    for b in range(2):
+        for t in range(3):
+            exact = [float(sum(Fraction(int(h[b, t, c])) * Fraction(int(round(w_dkv[r, c] * 64)), 64) for c in range(d)))
+                     for r in range(dc)]
+            # the exact sums fit float32; torch's cast rounds them to bf16 (nearest-even)
+            lib = torch.tensor(exact, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+            err = max(err, float(np.max(np.abs(rows[b, t, :dc] - lib))))
+            if pos[b, t] == 0:
+                kr = [float(sum(Fraction(int(h[b, t, c])) * Fraction(int(round(w_kr[r, c] * 64)), 64) for c in range(d)))
+                      for r in range(dr)]
+                lib = torch.tensor(kr, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+                err = max(err, float(np.max(np.abs(rows[b, t, dc:] - lib))))
+    pool = np.full((6, bs, dc + dr), -3.0)
+    bt = np.array([[4, 1, 5], [0, 3, 2]])
+    orc.write_rows(pool, bt, pos, rows, bs)
+    expect = np.full_like(pool, -3.0)
+    for b in range(2):
+        for t in range(3):
+            p = pos[b, t]
+            expect[bt[b, p // bs], p % bs] = rows[b, t]
+    err = max(err, float(np.max(np.abs(pool - expect))))
+    return err
+
+
+ALL_PINS = [
+    pin_bf16_rounding, pin_f32_rounding, pin_rope_rotation, pin_absorption, pin_mha_special_case,
+    pin_mqa_special_case, pin_softmax_normalised, pin_closed_forms, pin_causal_group, pin_paging,
+    pin_append_exact,
+]
+
+
+def pin_query_key_rotation_alignment(orc) -> float:
+    """The query projection and the append rotate by the same position: with
+    W^QR = W^KR (one head) and the same hidden state at position p, the rotary
+    score q^R . k^R equals |W^KR h|^2 (a rotation applied to both sides)."""
+    rng = _rng(12)
+    d, dr, dc = 10, 6, 4
+    w_kr = rng.standard_normal((dr, d))
+    w_dkv = rng.standard_normal((dc, d))
+    w_q = rng.standard_normal((3, d))
+    err = 0.0
+    for p in [0, 1, 7, 300, 8191]:
+        h = rng.standard_normal((1, 1, d))
+        pos = np.array([[p]])
+        row = orc.cache_rows(h, w_dkv, w_kr, pos, 10000.0, "f64")
+        _, qr = orc.q_project(h, w_q, w_kr, pos, 1, 10000.0)
+        want = float(np.sum((w_kr @ h[0, 0]) ** 2))
+        err = max(err, abs(float(qr[0, 0, 0] @ row[0, 0, dc:]) - want) / want)
+    return err
+
+
+ALL_PINS.append(pin_query_key_rotation_alignment)
