@@ -1,0 +1,186 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) MLA decode library.
+ *
+ * Multi-head Latent Attention decode over a paged latent KV cache.  Each cached
+ * token keeps only its joint latent c^KV (d_latent wide) followed by its
+ * rotary key k^R (d_rope wide), as "DeepSeek-V2: Multi-Head Latent Attention
+ * (MLA) 原理与工程实现" §2.1 (joint low-rank K/V compression) and §3.3 (cache of
+ * d_c + d_h^R per token) describe.  Decode runs in latent space through matrix
+ * absorption (same page, §2.2): every head's q^C is turned into a latent query
+ * with W^UK_i, scored against [c^KV ‖ k^R] together with the rotated q^R
+ * (§3.2, decoupled RoPE), the softmax weights sum the latents, and W^UV_i
+ * restores the head's output.
+ *
+ * Conventions for every entry point
+ *  - Return 0 (MLA_OK) or a negative MLA_ERR_* code.  All shape, dtype,
+ *    pointer and alignment errors are found on the host before anything is
+ *    launched; on error nothing is launched and no memory is touched.
+ *  - Array pointers are DEVICE pointers owned by the caller (unless a comment
+ *    says host).  The library never allocates, frees or synchronises; every
+ *    launch is asynchronous on the caller's stream (`stream` is a hipStream_t,
+ *    NULL = the default stream).
+ *  - Arrays are dense, row-major, in the element type named by dims->dtype
+ *    (MLA_DTYPE_F32: float, MLA_DTYPE_BF16: bfloat16) unless typed int32/float.
+ *    Device arrays must be 16-byte aligned.
+ *  - Weights are stored out x in, as the page writes W in R^{out x in}.
+ *  - Problems that only the data can reveal (a block id outside the pool, a
+ *    sequence longer than its block-table row, an append position outside
+ *    its table row) are never turned into out-of-bounds accesses: the access
+ *    is clamped or skipped and the matching MLA_STATUS_* bit is OR-ed into
+ *    the optional device word `status`.
+ *  - The library holds no mutable global state; concurrent calls on different
+ *    streams are safe as long as they do not share output or workspace memory.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define MLA_OK                        0
+#define MLA_ERR_NULL_PTR             -1  /* a required pointer is NULL */
+#define MLA_ERR_BAD_DIMS             -2  /* a size is out of range or inconsistent */
+#define MLA_ERR_BAD_DTYPE            -3  /* dims->dtype is not a known type */
+#define MLA_ERR_BAD_ALIGN            -4  /* a device pointer is not 16-byte aligned */
+#define MLA_ERR_WORKSPACE_TOO_SMALL  -5  /* workspace_bytes < mla_decode_workspace_bytes(...) */
+#define MLA_ERR_CAPACITY             -6  /* a size exceeds what the kernels index (see below) */
+#define MLA_ERR_HIP                  -7  /* the HIP runtime refused a launch */
+#define MLA_ERR_UNSUPPORTED          -8  /* valid dims that the bf16 kernels are not built for */
+
+/* bits OR-ed into *status by the kernels */
+#define MLA_STATUS_BAD_BLOCK   0x1  /* block_table named a block outside [0, num_blocks) */
+#define MLA_STATUS_BAD_LENGTH  0x2  /* seq_lens[b] < sq or > max_blocks * block_size */
+#define MLA_STATUS_BAD_POS     0x4  /* append position < 0 or >= max_blocks * block_size */
+
+#define MLA_DTYPE_F32   0
+#define MLA_DTYPE_BF16  1
+
+/* Model dimensions (names follow the DeepSeek-V2 MLA page's notation). */
+typedef struct mla_dims {
+  int32_t n_heads;     /* n_h                                                   */
+  int32_t d_nope;      /* d_h: per-head width of q^C, k^C and v                 */
+  int32_t d_rope;      /* d_h^R: width of the decoupled rotary q^R_i and k^R    */
+  int32_t d_latent;    /* d_c: width of the joint latent c^KV                   */
+  int32_t d_model;     /* d: hidden size the down-projections read              */
+  int32_t block_size;  /* tokens per cache block                                */
+  int32_t dtype;       /* MLA_DTYPE_F32 or MLA_DTYPE_BF16                       */
+  float rope_base;     /* RoPE base b: pair i turns by pos * b^(-2i/d_rope)     */
+} mla_dims;
+
+/*
+ * Size limits.
+ *  - MLA_DTYPE_BF16 runs the MFMA kernels, built for DeepSeek-V2's widths:
+ *    d_nope = 128, d_rope = 64, d_latent = 512, block_size = 64, n_heads a
+ *    multiple of 16 up to 128, d_model a multiple of 64, sq in 1..8.  Other
+ *    bf16 dims give MLA_ERR_UNSUPPORTED.
+ *  - MLA_DTYPE_F32 runs plain fp32 kernels for any dims with d_nope, d_rope
+ *    (even) and d_latent in 1..1024, d_latent + d_rope <= 1024,
+ *    n_heads <= 1024, block_size 1..1024, sq in 1..64.
+ *  - batch <= 65536; num_blocks * block_size * (d_latent + d_rope) < 2^40.
+ */
+
+/* A short English description of a return code (static storage; never NULL). */
+const char* mla_status_str(int code);
+
+/*
+ * Bytes the latent cache needs for `tokens` tokens: tokens * (d_latent + d_rope)
+ * * sizeof(dtype) ("DeepSeek-V2 ... MLA" page §3.3: d_c + d_h^R elements per
+ * token per layer, against MHA's 2 n_h d_h in §1.1).  Returns 0 for invalid dims
+ * or a negative token count.  Pure host arithmetic.
+ */
+size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens);
+
+/*
+ * Append `t` new tokens per sequence to the paged latent cache.
+ *
+ * For token (b, j) at position p = positions[b*t + j] with hidden state
+ * h[b, j, :] (d_model wide):
+ *   c   = W^DKV h                    (W^DKV: w_dkv [d_latent, d_model])  §2.1
+ *   k^R = RoPE_p(W^KR h)             (W^KR:  w_kr  [d_rope,   d_model])  §3.2
+ *   cache[block_table[b*max_blocks + p / block_size]][p % block_size][:]
+ *       = [c ‖ k^R] rounded to dtype (bf16: nearest-even)
+ * RoPE turns pairs (x_{2i}, x_{2i+1}) by angle p * rope_base^(-2i/d_rope); the
+ * angle and its sine/cosine are evaluated in fp64.
+ * Dot products accumulate in fp32.  Exactly batch*t rows of d_latent + d_rope
+ * elements are written and nothing else.  The caller advances its seq_lens.
+ *
+ * h          [batch, t, d_model]            dtype
+ * w_dkv      [d_latent, d_model]            dtype
+ * w_kr       [d_rope, d_model]              dtype
+ * positions  [batch, t]                     int32 (device)
+ * block_table[batch, max_blocks]            int32 (device)
+ * cache      [num_blocks, block_size, d_latent + d_rope]  dtype, written in place
+ * status     optional int32 (device), OR-ed with MLA_STATUS_BAD_POS/BAD_BLOCK; a
+ *            row whose position or block is invalid is skipped.
+ */
+int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr,
+                     const int32_t* positions, const int32_t* block_table, int32_t max_blocks,
+                     void* cache, int32_t num_blocks, int32_t batch, int32_t t,
+                     int32_t* status, void* stream);
+
+/*
+ * Project the query hidden states of `sq` tokens per sequence:
+ *   q_nope[b, s, i, :] = W^Q_i h[b, s, :]            (w_q  [n_heads*d_nope, d_model])
+ *   q_rope[b, s, i, :] = RoPE_p(W^QR_i h[b, s, :])   (w_qr [n_heads*d_rope, d_model])
+ * with p = positions[b*sq + s] ("DeepSeek-V2 ... MLA" page §1.1 for W^Q on h,
+ * §3.2 for the multi-head rotary query).  Same RoPE and accumulation rules as
+ * mla_cache_append.  Outputs are in dtype.
+ */
+int mla_q_project(const mla_dims* dims, const void* h, const void* w_q, const void* w_qr,
+                  const int32_t* positions, void* q_nope, void* q_rope,
+                  int32_t batch, int32_t sq, void* stream);
+
+/*
+ * Workspace bytes mla_decode needs for this batch shape.  num_splits is the
+ * number of attention workgroups the token space is cut into (0 = one per
+ * compute unit of the current device); pass the same value to mla_decode.
+ * Returns 0 for invalid arguments.
+ */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t sq, int32_t num_splits);
+
+/*
+ * Decode attention for `sq` query tokens per sequence ("DeepSeek-V2 ... MLA"
+ * page §2.2 absorption and §3.2 decoupled RoPE):
+ *   q~_i   = W^UK_i^T q^C_i                     latent query, d_latent wide
+ *   z_j    = scale * ([q~_i ‖ q^R_i] . [c_j ‖ k^R_j])
+ *   p      = softmax over the visible tokens j
+ *   out_i  = W^UV_i (sum_j p_j c_j)
+ * W^UK_i, W^UV_i are rows i*d_nope .. (i+1)*d_nope-1 of w_uk, w_uv.
+ * Query s of sequence b sits at position seq_lens[b] - sq + s and sees cached
+ * tokens 0 .. seq_lens[b] - sq + s (itself included; causal inside the group).
+ * The token space is cut into num_splits equal ranges processed in parallel;
+ * the partial softmax states are merged exactly by log-sum-exp.
+ *
+ * q_nope     [batch, sq, n_heads, d_nope]   dtype
+ * q_rope     [batch, sq, n_heads, d_rope]   dtype, already rotated
+ * w_uk, w_uv [n_heads*d_nope, d_latent]     dtype
+ * cache      [num_blocks, block_size, d_latent + d_rope]  dtype
+ * block_table[batch, max_blocks]            int32 (device)
+ * seq_lens   [batch]                        int32 (device), query tokens included
+ * softmax_scale  e.g. 1/sqrt(d_nope + d_rope)
+ * num_splits 0 = one attention workgroup per compute unit; >0 forces the count
+ * workspace  device scratch of at least mla_decode_workspace_bytes(dims, batch,
+ *            sq, num_splits) bytes, 256-byte aligned; its contents on entry do
+ *            not matter and are clobbered
+ * out        [batch, sq, n_heads, d_nope]   dtype
+ * lse        optional [batch, sq, n_heads] float: natural log of sum_j exp(z_j);
+ *            -inf (and out = 0) for a query that sees no token
+ * status     optional int32 (device), OR-ed with MLA_STATUS_BAD_BLOCK/BAD_LENGTH
+ */
+int mla_decode(const mla_dims* dims, const void* q_nope, const void* q_rope,
+               const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+               const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+               int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
+               void* workspace, size_t workspace_bytes, void* out, float* lse,
+               int32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,220 @@
+// Host entry points of the MLA decode library (the C ABI declared in mla.h).
+// Every check that the arguments allow is made here, before anything is
+// launched; the kernels only guard against what the data alone can reveal.
+#include <atomic>
+#include <cmath>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == MLA_DTYPE_BF16 ? 2 : 4; }
+
+// Checks that hold for every entry point.
+int check_dims(const mla_dims* d) {
+  if (d == nullptr) return MLA_ERR_NULL_PTR;
+  if (d->dtype != MLA_DTYPE_F32 && d->dtype != MLA_DTYPE_BF16) return MLA_ERR_BAD_DTYPE;
+  if (d->n_heads < 1 || d->d_nope < 1 || d->d_rope < 0 || d->d_latent < 1 || d->d_model < 1 || d->block_size < 1)
+    return MLA_ERR_BAD_DIMS;
+  if (d->d_rope % 2 != 0) return MLA_ERR_BAD_DIMS;   // RoPE turns pairs
+  if (!(d->rope_base > 0.0f) || !std::isfinite(d->rope_base)) return MLA_ERR_BAD_DIMS;
+  if (d->dtype == MLA_DTYPE_BF16) {
+    if (d->d_nope != kNope || d->d_rope != kRope || d->d_latent != kLat || d->block_size != kBlk)
+      return MLA_ERR_UNSUPPORTED;
+    if (d->n_heads > 1024 || d->d_model % 32 != 0) return MLA_ERR_UNSUPPORTED;
+  } else {
+    if (d->d_nope > kF32MaxWidth || d->d_latent > kF32MaxWidth || d->d_latent + d->d_rope > kF32MaxWidth ||
+        d->n_heads > 1024 || d->block_size > 1024)
+      return MLA_ERR_CAPACITY;
+  }
+  if (d->d_model > (1 << 20)) return MLA_ERR_CAPACITY;
+  return MLA_OK;
+}
+
+int check_sq(const mla_dims* d, int sq) {
+  if (sq < 1) return MLA_ERR_BAD_DIMS;
+  if (sq > (d->dtype == MLA_DTYPE_BF16 ? kMaxSqBf16 : kF32MaxSq)) return MLA_ERR_CAPACITY;
+  if (d->dtype == MLA_DTYPE_F32 && d->n_heads * sq > 65535) return MLA_ERR_CAPACITY;   // one grid row per query row
+  return MLA_OK;
+}
+
+int check_pool(const mla_dims* d, int num_blocks, int max_blocks, int batch) {
+  if (num_blocks < 1 || max_blocks < 1 || batch < 1) return MLA_ERR_BAD_DIMS;
+  if (batch > 65536) return MLA_ERR_CAPACITY;
+  const long long R = d->d_latent + d->d_rope;
+  if ((long long)num_blocks * d->block_size >= (1ll << 31)) return MLA_ERR_CAPACITY;
+  if ((long long)num_blocks * d->block_size * R >= (1ll << 40)) return MLA_ERR_CAPACITY;
+  if ((long long)batch * max_blocks >= (1ll << 31)) return MLA_ERR_CAPACITY;
+  if ((long long)batch * max_blocks * d->block_size >= (1ll << 31)) return MLA_ERR_CAPACITY;
+  return MLA_OK;
+}
+
+std::atomic<int> g_cus[64];
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+  if (dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L) {
+  const bool bf = d->dtype == MLA_DTYPE_BF16;
+  if (bf) {
+    L->hg = d->n_heads < kRowsWG / sq ? d->n_heads : kRowsWG / sq;
+    L->G = (d->n_heads + L->hg - 1) / L->hg;
+    L->rows = kRowsWG;
+    L->align = kBlk;
+  } else {
+    L->hg = d->n_heads;
+    L->G = 1;
+    L->rows = d->n_heads * sq;
+    L->align = 16;
+  }
+  int W = num_splits;
+  if (W <= 0) {
+    int cus = device_cu_count();
+    if (cus <= 0) return false;
+    W = bf ? (cus / L->G > 0 ? cus / L->G : 1) : cus;
+  }
+  if (W > (1 << 20)) return false;
+  L->W = W;
+  L->P = W + batch;
+  const size_t R = (size_t)d->d_latent + d->d_rope;
+  size_t off = 0;
+  L->off_hdr = off;   off += up(sizeof(PlanHeader));
+  L->off_seg = off;   off += up((size_t)(batch + 1) * 4);
+  L->off_piece = off; off += up((size_t)(batch + 1) * 4);
+  L->off_wgseg = off; off += up((size_t)W * 4);
+  L->off_qlat = off;  off += up((size_t)batch * sq * d->n_heads * R * elem_size(d->dtype));
+  L->off_lse = off;   off += up((size_t)L->G * L->P * L->rows * 8);
+  L->off_o = off;     off += up((size_t)L->G * L->P * L->rows * d->d_latent * 4);
+  L->total = off;
+  return true;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char* mla_status_str(int code) {
+  switch (code) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MLA_ERR_BAD_DIMS: return "a size is out of range or inconsistent";
+    case MLA_ERR_BAD_DTYPE: return "unknown element type";
+    case MLA_ERR_BAD_ALIGN: return "a device pointer is not 16-byte aligned (workspace: 256-byte)";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_decode_workspace_bytes()";
+    case MLA_ERR_CAPACITY: return "a size exceeds what the kernels can index";
+    case MLA_ERR_HIP: return "the HIP runtime refused a launch";
+    case MLA_ERR_UNSUPPORTED: return "dims the bf16 kernels are not built for";
+    default: return "unknown status code";
+  }
+}
+
+size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens) {
+  if (check_dims(dims) != MLA_OK || tokens < 0) return 0;
+  return (size_t)tokens * ((size_t)dims->d_latent + dims->d_rope) * elem_size(dims->dtype);
+}
+
+int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr, const int32_t* positions,
+                     const int32_t* block_table, int32_t max_blocks, void* cache, int32_t num_blocks, int32_t batch,
+                     int32_t t, int32_t* status, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if (!h || !w_dkv || !w_kr || !positions || !block_table || !cache) return MLA_ERR_NULL_PTR;
+  if (t < 1) return MLA_ERR_BAD_DIMS;
+  if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
+  if ((long long)batch * t >= (1ll << 30)) return MLA_ERR_CAPACITY;
+  if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(positions) || !aligned16(block_table) ||
+      !aligned16(cache) || (status && ((uintptr_t)status & 3u)))
+    return MLA_ERR_BAD_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (dims->dtype == MLA_DTYPE_BF16)
+    e = launch_append_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions, block_table,
+                           max_blocks, (uint16_t*)cache, num_blocks, batch * t, t, dims->d_model, dims->rope_base,
+                           status, st);
+  else
+    e = launch_append_f32(dims, (const float*)h, (const float*)w_dkv, (const float*)w_kr, positions, block_table,
+                          max_blocks, (float*)cache, num_blocks, batch * t, t, status, st);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_q_project(const mla_dims* dims, const void* h, const void* w_q, const void* w_qr, const int32_t* positions,
+                  void* q_nope, void* q_rope, int32_t batch, int32_t sq, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if (!h || !w_q || !positions || !q_nope || ((!w_qr || !q_rope) && dims->d_rope > 0)) return MLA_ERR_NULL_PTR;
+  if (batch < 1 || sq < 1) return MLA_ERR_BAD_DIMS;
+  if ((long long)batch * sq * dims->n_heads * (dims->d_nope + dims->d_rope) >= (1ll << 31)) return MLA_ERR_CAPACITY;
+  if (!aligned16(h) || !aligned16(w_q) || (w_qr && !aligned16(w_qr)) || !aligned16(positions) ||
+      !aligned16(q_nope) || (q_rope && !aligned16(q_rope)))
+    return MLA_ERR_BAD_ALIGN;
+  hipError_t e = launch_qproj(dims, h, w_q, w_qr, positions, q_nope, q_rope, batch * sq, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t sq, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || check_sq(dims, sq) != MLA_OK || batch < 1 || batch > 65536 || num_splits < 0)
+    return 0;
+  WsLayout L;
+  if (!ws_layout(dims, batch, sq, num_splits, &L)) return 0;
+  return L.total;
+}
+
+int mla_decode(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+               const void* cache, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+               const int32_t* seq_lens, int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
+               void* workspace, size_t workspace_bytes, void* out, float* lse, int32_t* status, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if (!q_nope || !w_uk || !w_uv || !cache || !block_table || !seq_lens || !workspace || !out) return MLA_ERR_NULL_PTR;
+  if (dims->d_rope > 0 && !q_rope) return MLA_ERR_NULL_PTR;
+  if ((rc = check_sq(dims, sq)) != MLA_OK) return rc;
+  if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
+  if (num_splits < 0 || !std::isfinite(softmax_scale)) return MLA_ERR_BAD_DIMS;
+  if (!aligned16(q_nope) || (q_rope && !aligned16(q_rope)) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(cache) || !aligned16(block_table) || !aligned16(seq_lens) || !aligned16(out) ||
+      ((uintptr_t)workspace & (kAlign - 1)) || (lse && ((uintptr_t)lse & 3u)) || (status && ((uintptr_t)status & 3u)))
+    return MLA_ERR_BAD_ALIGN;
+  WsLayout L;
+  if (!ws_layout(dims, batch, sq, num_splits, &L)) return MLA_ERR_HIP;
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  hipError_t e;
+  if (dims->dtype == MLA_DTYPE_BF16) {
+    e = launch_absorb_bf16(L, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens,
+                           max_blocks, batch, sq, dims->n_heads, ws, status, st);
+    if (e == hipSuccess)
+      e = launch_attn_bf16(L, (const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq,
+                           dims->n_heads, softmax_scale, ws, status, st);
+    if (e == hipSuccess)
+      e = launch_merge_upv_bf16(L, (const uint16_t*)w_uv, batch, sq, dims->n_heads, ws, (uint16_t*)out, lse, st);
+  } else {
+    e = launch_decode_f32(dims, L, (const float*)q_nope, (const float*)q_rope, (const float*)w_uk, (const float*)w_uv,
+                          (const float*)cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq, softmax_scale,
+                          ws, (float*)out, lse, status, st);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Internal declarations shared by the HIP kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// Fixed widths of the bf16 MFMA kernels (DeepSeek-V2's MLA: d_c = 512,
+// d_h^R = 64, d_h = 128, as the DeepSeek-V2 MLA page gives in §1.1 and §3.3).
+// ---------------------------------------------------------------------------
+constexpr int kLat = 512;            // d_latent
+constexpr int kRope = 64;            // d_rope
+constexpr int kRow = kLat + kRope;   // cached row: [c^KV ‖ k^R]
+constexpr int kNope = 128;           // d_nope
+constexpr int kBlk = 64;             // tokens per cache block
+constexpr int kRowsWG = 128;         // query rows (head, query-token) per attention workgroup
+constexpr int kSubTok = 32;          // tokens per LDS stage
+constexpr int kStages = 4;           // LDS ring depth
+constexpr int kStageBytes = kSubTok * kRow * 2;        // 36864
+constexpr int kChunksPerRow = kRow * 2 / 16;           // 72 chunks of 16 B
+constexpr int kMaxSqBf16 = 8;
+
+// f32 generic path limits
+constexpr int kF32MaxWidth = 1024;
+constexpr int kF32MaxSq = 64;
+
+// ---------------------------------------------------------------------------
+// Split plan.  The per-group token space is the concatenation over sequences
+// of seq_len rounded up to `align`; it is cut into `num_wg` equal ranges of
+// `quota` tokens.  Every (range, sequence) intersection is one piece with its
+// own partial softmax state.  Written on the device by plan_build().
+// ---------------------------------------------------------------------------
+struct PlanHeader {
+  int32_t total;      // tokens in the (rounded) space of one head group
+  int32_t quota;      // tokens per range (multiple of align)
+  int32_t pieces;     // pieces per head group
+  int32_t status;     // reserved
+};
+
+// Workspace layout, computed identically by the size query and by decode.
+struct WsLayout {
+  int G;              // head groups
+  int hg;             // heads per group
+  int rows;           // query rows per group (padded for bf16)
+  int W;              // ranges (workgroups) per head group
+  int P;              // max pieces per head group = W + batch
+  int align;          // token alignment of ranges
+  size_t off_hdr, off_seg, off_piece, off_wgseg, off_qlat, off_lse, off_o, total;
+};
+
+bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L);
+int device_cu_count();
+
+// ---------------------------------------------------------------------------
+// Launchers (one per kernel family).  Each returns hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+hipError_t launch_append_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
+                              const int32_t* positions, const int32_t* block_table, int max_blocks,
+                              uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
+                              float rope_base, int32_t* status, hipStream_t st);
+hipError_t launch_append_f32(const mla_dims* d, const float* h, const float* w_dkv, const float* w_kr,
+                             const int32_t* positions, const int32_t* block_table, int max_blocks,
+                             float* cache, int num_blocks, int tokens, int t_per_seq,
+                             int32_t* status, hipStream_t st);
+hipError_t launch_qproj(const mla_dims* d, const void* h, const void* w_q, const void* w_qr,
+                        const int32_t* positions, void* q_nope, void* q_rope, int tokens, hipStream_t st);
+hipError_t launch_absorb_bf16(const WsLayout& L, const uint16_t* q_nope, const uint16_t* q_rope,
+                              const uint16_t* w_uk, const int32_t* seq_lens, int max_blocks, int batch,
+                              int sq, int n_heads, uint8_t* ws, int32_t* status, hipStream_t st);
+hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_blocks,
+                            const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
+                            int batch, int sq, int n_heads, float scale, uint8_t* ws, int32_t* status,
+                            hipStream_t st);
+hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads,
+                                 uint8_t* ws, uint16_t* out, float* lse, hipStream_t st);
+hipError_t launch_decode_f32(const mla_dims* d, const WsLayout& L, const float* q_nope, const float* q_rope,
+                             const float* w_uk, const float* w_uv, const float* cache, int num_blocks,
+                             const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
+                             int batch, int sq, float scale, uint8_t* ws, float* out, float* lse,
+                             int32_t* status, hipStream_t st);
+
+}  // namespace mla

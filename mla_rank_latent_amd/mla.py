@@ -1,0 +1,127 @@
+"""Python binding of the MLA decode library (``include/mla.h``).
+
+Argument marshalling only: each function takes torch tensors, reads their
+device pointers and shapes, and calls the C entry point of the same name.
+Every step of the computation runs in the library's HIP kernels.  Importing
+this module loads ``libmla_rank_latent.so`` and raises ImportError if it is
+missing; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_rank_latent.so")
+
+MLA_DTYPE_F32 = 0
+MLA_DTYPE_BF16 = 1
+MLA_STATUS_BAD_BLOCK = 0x1
+MLA_STATUS_BAD_LENGTH = 0x2
+MLA_STATUS_BAD_POS = 0x4
+
+EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_q_project",
+           "mla_decode_workspace_bytes", "mla_decode")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or python -m mla_rank_latent_amd.build)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_model", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_lib.mla_status_str.restype = ctypes.c_char_p
+_lib.mla_status_str.argtypes = [ctypes.c_int]
+_lib.mla_cache_bytes.restype = ctypes.c_size_t
+_lib.mla_cache_bytes.argtypes = [ctypes.POINTER(MlaDims), ctypes.c_int64]
+_lib.mla_cache_append.restype = ctypes.c_int
+_lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P]
+_lib.mla_q_project.restype = ctypes.c_int
+_lib.mla_q_project.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I, _I, _P]
+_lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I, _I]
+_lib.mla_decode.restype = ctypes.c_int
+_lib.mla_decode.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _I,
+                            _P, ctypes.c_size_t, _P, _P, _P, _P]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {code}: {mla_status_str(code)}")
+        self.code = code
+
+
+def dims(n_heads: int, d_nope: int, d_rope: int, d_latent: int, d_model: int, block_size: int = 64,
+         dtype: str = "bf16", rope_base: float = 10000.0) -> MlaDims:
+    return MlaDims(n_heads, d_nope, d_rope, d_latent, d_model, block_size,
+                   MLA_DTYPE_BF16 if dtype == "bf16" else MLA_DTYPE_F32, rope_base)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MlaError(fn, rc)
+
+
+def mla_status_str(code: int) -> str:
+    return _lib.mla_status_str(code).decode()
+
+
+def mla_cache_bytes(d: MlaDims, tokens: int) -> int:
+    return int(_lib.mla_cache_bytes(ctypes.byref(d), tokens))
+
+
+def mla_decode_workspace_bytes(d: MlaDims, batch: int, sq: int, num_splits: int = 0) -> int:
+    return int(_lib.mla_decode_workspace_bytes(ctypes.byref(d), batch, sq, num_splits))
+
+
+def mla_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, status=None, stream=None) -> None:
+    """h [batch, t, d_model]; positions [batch, t] int32; block_table [batch, max_blocks] int32;
+    cache [num_blocks, block_size, d_latent + d_rope] (written in place)."""
+    batch, t = int(h.shape[0]), int(h.shape[1])
+    _check("mla_cache_append", _lib.mla_cache_append(
+        ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(positions), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(cache), int(cache.shape[0]), batch, t, _ptr(status), _stream(stream)))
+
+
+def mla_q_project(d: MlaDims, h, w_q, w_qr, positions, q_nope, q_rope, stream=None) -> None:
+    """h [batch, sq, d_model]; q_nope [batch, sq, n_heads, d_nope] and q_rope [batch, sq, n_heads, d_rope] written."""
+    batch, sq = int(h.shape[0]), int(h.shape[1])
+    _check("mla_q_project", _lib.mla_q_project(
+        ctypes.byref(d), _ptr(h), _ptr(w_q), _ptr(w_qr), _ptr(positions), _ptr(q_nope), _ptr(q_rope),
+        batch, sq, _stream(stream)))
+
+
+def mla_decode(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,
+               workspace, out, lse=None, status=None, num_splits: int = 0, stream=None) -> None:
+    """q_nope [batch, sq, n_heads, d_nope]; q_rope [batch, sq, n_heads, d_rope] (rotated);
+    out [batch, sq, n_heads, d_nope] and optional lse [batch, sq, n_heads] float32 written.
+    ``workspace`` is a byte tensor of at least mla_decode_workspace_bytes(d, batch, sq, num_splits)."""
+    batch, sq = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _check("mla_decode", _lib.mla_decode(
+        ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, sq, float(softmax_scale), num_splits,
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse), _ptr(status),
+        _stream(stream)))
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded shared library (tests call its entry points directly)."""
+    return _lib

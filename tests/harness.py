@@ -1,0 +1,184 @@
+"""Shared helpers for the GPU tests: move generated inputs to the device, run the
+library through its binding, and evaluate the oracle on the same inputs."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+from mla_rank_latent_amd import synth
+from oracle import mla_oracle
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, dtype: str):
+    """numpy array -> torch device tensor; bf16 bit patterns become torch.bfloat16."""
+    import torch
+    if x.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to("cuda")
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def mla_dims(spec: synth.Spec):
+    from mla_rank_latent_amd import mla
+    return mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, spec.dtype,
+                    spec.rope_base)
+
+
+class GpuCase:
+    """Device copies of one generated workload, plus the calls of one decode step."""
+
+    def __init__(self, x: dict, num_splits: int = 0):
+        import torch
+        from mla_rank_latent_amd import mla
+        self.x = x
+        self.spec = spec = x["spec"]
+        self.d = mla_dims(spec)
+        self.num_splits = num_splits
+        self.pool = dev(x["pool"], spec.dtype)
+        self.block_table = dev(x["block_table"], spec.dtype)
+        self.seq_lens = dev(x["seq_lens"], spec.dtype)
+        self.w_uk = dev(x["w_uk"], spec.dtype)
+        self.w_uv = dev(x["w_uv"], spec.dtype)
+        B, S, H = spec.batch, spec.sq, spec.n_heads
+        tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+        if spec.q_from_hidden:
+            self.q_nope = torch.empty(B, S, H, spec.d_nope, dtype=tdt, device="cuda")
+            self.q_rope = torch.empty(B, S, H, spec.d_rope, dtype=tdt, device="cuda")
+        else:
+            self.q_nope = dev(x["q_nope"], spec.dtype)
+            self.q_rope = dev(x["q_rope"], spec.dtype)
+        if "h" in x:
+            self.h = dev(x["h"], spec.dtype)
+            self.w_dkv = dev(x["w_dkv"], spec.dtype)
+            self.w_kr = dev(x["w_kr"], spec.dtype)
+            self.positions = dev(x["positions"], spec.dtype)
+        if spec.q_from_hidden:
+            self.w_q = dev(x["w_q"], spec.dtype)
+            self.w_qr = dev(x["w_qr"], spec.dtype)
+            self.q_positions = dev(x["q_positions"], spec.dtype)
+            self.h_q = self.h[:, -S:].contiguous()
+        self.out = torch.empty(B, S, H, spec.d_nope, dtype=tdt, device="cuda")
+        self.lse = torch.empty(B, S, H, dtype=torch.float32, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nbytes = mla.mla_decode_workspace_bytes(self.d, B, S, num_splits)
+        assert nbytes > 0
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def append(self):
+        from mla_rank_latent_amd import mla
+        mla.mla_cache_append(self.d, self.h, self.w_dkv, self.w_kr, self.positions, self.block_table, self.pool,
+                             status=self.status)
+
+    def q_project(self):
+        from mla_rank_latent_amd import mla
+        mla.mla_q_project(self.d, self.h_q, self.w_q, self.w_qr, self.q_positions, self.q_nope, self.q_rope)
+
+    def decode(self, num_splits=None):
+        from mla_rank_latent_amd import mla
+        mla.mla_decode(self.d, self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.pool, self.block_table,
+                       self.seq_lens, self.x["scale"], self.ws, self.out, lse=self.lse, status=self.status,
+                       num_splits=self.num_splits if num_splits is None else num_splits)
+
+    def step(self):
+        """One pass of the hot path: append (if the workload has one), project (tiny case), decode."""
+        if self.spec.append or self.spec.q_from_hidden:
+            self.append()
+        if self.spec.q_from_hidden:
+            self.q_project()
+        self.decode()
+
+
+# ---------------------------------------------------------------------------
+# oracle side
+# ---------------------------------------------------------------------------
+def oracle_append_rows(x: dict) -> np.ndarray:
+    spec = x["spec"]
+    return mla_oracle.cache_rows(synth.as_float(x["h"], spec.dtype), synth.as_float(x["w_dkv"], spec.dtype),
+                                 synth.as_float(x["w_kr"], spec.dtype), x["positions"], spec.rope_base, spec.dtype)
+
+
+def oracle_decode(x: dict, batches=None, heads=None, appended_rows=None, q=None):
+    """Oracle output for the sampled sequences/heads.  ``appended_rows`` [B, T, R]
+    are the oracle's own rows for the append positions (so the oracle never
+    reads a value the GPU wrote); ``q`` overrides (q_nope, q_rope) as float64."""
+    spec = x["spec"]
+    B, bs = spec.batch, spec.block_size
+    batches = list(range(B)) if batches is None else list(batches)
+    if q is None:
+        qn, qr = synth.as_float(x["q_nope"], spec.dtype), synth.as_float(x["q_rope"], spec.dtype)
+    else:
+        qn, qr = q
+    w_uk, w_uv = synth.as_float(x["w_uk"], spec.dtype), synth.as_float(x["w_uv"], spec.dtype)
+    out = np.full(qn.shape, np.nan)
+    lse = np.full(qn.shape[:3], np.nan)
+    for b in batches:
+        L = int(x["seq_lens"][b])
+        nblk = (L + bs - 1) // bs
+        sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)   # this sequence's blocks, in order
+        if appended_rows is not None:
+            for t, p in enumerate(x["positions"][b]):
+                sub[p // bs, p % bs] = appended_rows[b, t]
+        o, l = mla_oracle.decode(qn[b:b + 1], qr[b:b + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :], [L],
+                                 x["scale"], bs, heads=heads)
+        out[b], lse[b] = o[0], l[0]
+    return out, lse
+
+
+def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:
+    m = ~np.isnan(ref)
+    return float(np.linalg.norm((a - ref)[m]) / max(np.linalg.norm(ref[m]), 1e-300))
+
+
+def max_abs(a: np.ndarray, ref: np.ndarray) -> float:
+    m = ~np.isnan(ref)
+    return float(np.max(np.abs((a - ref)[m]))) if m.any() else 0.0
+
+
+# spec tolerances: bf16 rel-L2 <= 1e-2 and max-abs <= 2e-2; fp32 rel-L2 <= 1e-4
+def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> None:
+    r = rel_l2(gpu, ref)
+    a = max_abs(gpu, ref)
+    log(f"  {what}: rel_l2={r:.3e} max_abs={a:.3e}")
+    if dtype == "bf16":
+        assert r <= 1e-2 and a <= 2e-2, (what, r, a)
+    else:
+        assert r <= 1e-4, (what, r, a)
+
+
+def small_spec(name, batch, sq, lens, paged=True, append=False, seed=11, n_heads=128, d_model=5120):
+    return synth.Spec(name, batch=batch, sq=sq, seq_lens=list(lens), paged=paged, append=append, seed=seed,
+                      n_heads=n_heads, d_model=d_model)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (for 1-ulp comparisons)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def lse_probability_sum(x: dict, b: int, s: int, h: int, lse: float) -> float:
+    """sum_j exp(z_j - lse) over the visible tokens, with z from the oracle's decompressed logits."""
+    spec = x["spec"]
+    bs = spec.block_size
+    L = int(x["seq_lens"][b])
+    rows = mla_oracle.gather_rows(synth.as_float(x["pool"], spec.dtype), x["block_table"][b], L, bs)
+    dc, dn = spec.d_latent, spec.d_nope
+    wk = synth.as_float(x["w_uk"], spec.dtype)[h * dn:(h + 1) * dn]
+    k = np.concatenate([rows[:, :dc] @ wk.T, rows[:, dc:]], axis=1)
+    q = np.concatenate([synth.as_float(x["q_nope"], spec.dtype)[b, s, h], synth.as_float(x["q_rope"], spec.dtype)[b, s, h]])
+    n = L - spec.sq + s + 1
+    z = x["scale"] * (k[:n] @ q)
+    return float(np.sum(np.exp(z - lse)))

@@ -1,0 +1,107 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_rank_latent_amd import mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def test_exports_every_declared_function():
+    decl = re.findall(r"^\s*(?:const\s+char\*|size_t|int)\s+(mla_\w+)\s*\(", open(HEADER).read(), re.M)
+    assert sorted(decl) == sorted(mla.EXPORTS)
+    lib = mla.raw_library()
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8]
+    strs = [mla.mla_status_str(c) for c in codes]
+    assert len(set(strs)) == len(codes)
+    assert mla.mla_status_str(-99) == "unknown status code"
+
+
+def test_cache_bytes_accounting():
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    assert mla.mla_cache_bytes(v2, 1) == 576 * 2       # d_c + d_h^R elements in bf16
+    assert mla.mla_cache_bytes(v2, 8192 * 64) == 8192 * 64 * 1152
+    f32 = mla.dims(8, 16, 8, 32, 64, dtype="f32")
+    assert mla.mla_cache_bytes(f32, 65) == 65 * 40 * 4
+    assert mla.mla_cache_bytes(v2, -1) == 0
+    bad = mla.dims(128, 128, 64, 512, 5120)
+    bad.dtype = 7
+    assert mla.mla_cache_bytes(bad, 10) == 0
+
+
+def test_workspace_query():
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    w64 = mla.mla_decode_workspace_bytes(v2, 64, 1, 256)
+    # q_lat + (256 + 64) pieces x 128 rows x (512 floats + 2 floats) + plan
+    assert w64 >= 64 * 128 * 576 * 2 + 320 * 128 * 514 * 4
+    assert mla.mla_decode_workspace_bytes(v2, 64, 2, 128) > 0
+    assert mla.mla_decode_workspace_bytes(v2, 64, 9, 128) == 0     # sq beyond the bf16 kernels
+    assert mla.mla_decode_workspace_bytes(v2, 0, 1, 128) == 0
+    odd = mla.dims(128, 96, 64, 512, 5120)
+    assert mla.mla_decode_workspace_bytes(odd, 4, 1, 16) == 0      # bf16 widths are fixed
+
+
+FAKE = 0x10000   # aligned, never dereferenced: every call below fails validation first
+
+
+def _decode(d, **kw):
+    a = dict(q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE, cache=FAKE, num_blocks=16, block_table=FAKE,
+             max_blocks=4, seq_lens=FAKE, batch=4, sq=1, scale=0.1, num_splits=8, ws=FAKE, ws_bytes=1 << 40,
+             out=FAKE, lse=None, status=None, stream=None)
+    a.update(kw)
+    return mla.raw_library().mla_decode(ctypes.byref(d), a["q_nope"], a["q_rope"], a["w_uk"], a["w_uv"], a["cache"],
+                                        a["num_blocks"], a["block_table"], a["max_blocks"], a["seq_lens"],
+                                        a["batch"], a["sq"], a["scale"], a["num_splits"], a["ws"], a["ws_bytes"],
+                                        a["out"], a["lse"], a["status"], a["stream"])
+
+
+def test_decode_argument_errors():
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    assert _decode(v2, q_nope=None) == -1
+    assert _decode(v2, ws=None) == -1
+    assert _decode(v2, batch=0) == -2
+    assert _decode(v2, sq=0) == -2
+    assert _decode(v2, sq=9) == -6
+    assert _decode(v2, num_blocks=0) == -2
+    assert _decode(v2, num_splits=-1) == -2
+    assert _decode(v2, scale=float("nan")) == -2
+    assert _decode(v2, cache=FAKE + 8) == -4
+    assert _decode(v2, ws=FAKE + 16) == -4
+    assert _decode(v2, ws_bytes=1024) == -5
+    assert _decode(v2, batch=70000) == -6
+    bad = mla.dims(128, 128, 64, 512, 5120)
+    bad.dtype = 3
+    assert _decode(bad) == -3
+    assert _decode(mla.dims(128, 128, 64, 256, 5120)) == -8
+    assert _decode(mla.dims(128, 128, 64, 512, 5120, block_size=32)) == -8
+    assert _decode(mla.dims(8, 16, 7, 32, 64, dtype="f32")) == -2       # odd rotary width
+    assert _decode(mla.dims(8, 16, 8, 2048, 64, dtype="f32")) == -6
+
+
+def test_append_and_qproj_argument_errors():
+    lib = mla.raw_library()
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, 2, 1, None, None]
+    assert lib.mla_cache_append(ctypes.byref(v2), *args[:4], None, *args[5:]) == -1
+    bad_t = list(args)
+    bad_t[9] = 0
+    assert lib.mla_cache_append(ctypes.byref(v2), *bad_t) == -2
+    mis = list(args)
+    mis[0] = FAKE + 2
+    assert lib.mla_cache_append(ctypes.byref(v2), *mis) == -4
+    assert lib.mla_cache_append(ctypes.byref(mla.dims(128, 128, 64, 512, 5000)), *args) == -8
+    q = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, None]
+    assert lib.mla_q_project(ctypes.byref(v2), *q[:2], None, *q[3:]) == -1
+    q2 = list(q)
+    q2[6] = 0
+    assert lib.mla_q_project(ctypes.byref(v2), *q2) == -2
