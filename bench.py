@@ -1,0 +1,223 @@
+"""Benchmark of the MLA decode hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: append of the new
+token of every sequence (down-projection, RoPE, paged write), then decode
+(absorbed queries, split-KV latent attention, log-sum-exp merge, W^UV
+up-projection).  Default workload: batch 64, every sequence at context 8192
+after the append, 128 heads, DeepSeek-V2 widths, bf16 cache in 64-token
+blocks with a randomly permuted block table (seeded synthetic data).
+
+Prints one JSON line.  ``value`` is the whole step's algorithmic HBM
+throughput (bytes every step must move / step time).  ``roofline`` rates the
+dominant kernel (the split-KV attention) against the MI355X HBM peak, timed
+with HIP events around each of its launches on the stream it runs on.
+``cpu_baseline`` times the fp64 oracle on the host over a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+def workload_bytes_flops(spec, seq_lens):
+    """Algorithmic bytes and flops of one step, with their parts."""
+    H, dn, dr, dc, d = spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model
+    R = dc + dr
+    e = 2 if spec.dtype == "bf16" else 4
+    tokens = int(sum(int(L) for L in seq_lens))
+    B, S = spec.batch, spec.sq
+    cache = tokens * R * e                                  # every cached row read once
+    weights_dec = 2 * H * dn * dc * e                       # W^UK and W^UV
+    q_bytes = B * S * H * (dn + dr) * e
+    out_bytes = B * S * H * dn * e
+    append_bytes = 0
+    append_flops = 0
+    if spec.append:
+        append_bytes = (R * d + B * S * d + B * S * R) * e   # W^DKV, W^KR, h, written rows
+        append_flops = 2 * B * S * R * d
+    # scores over [c | k^R] (576) and the latent weighted sum (512) per visible token and query row
+    vis = 0
+    for L in seq_lens:
+        for s in range(S):
+            vis += max(0, int(L) - S + s + 1)
+    attn_flops = 2 * H * vis * (R + dc)
+    proj_flops = 2 * 2 * B * S * H * dn * dc                # absorption and up-projection
+    total_bytes = cache + weights_dec + q_bytes + out_bytes + append_bytes
+    total_flops = attn_flops + proj_flops + append_flops
+    return dict(bytes=total_bytes, flops=total_flops, cache_bytes=cache, attn_flops=attn_flops, tokens=tokens)
+
+
+def cpu_baseline(x, budget_s: float):
+    """Time the fp64 oracle (as it stands) on whole sequences of the workload until
+    ``budget_s`` of CPU work has been spent; scale to GB/s of the same algorithmic bytes."""
+    import numpy as np
+    from mla_rank_latent_amd import synth
+    from oracle import mla_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = x["spec"]
+    bs = spec.block_size
+    qn, qr = synth.as_float(x["q_nope"], spec.dtype), synth.as_float(x["q_rope"], spec.dtype)
+    w_uk, w_uv = synth.as_float(x["w_uk"], spec.dtype), synth.as_float(x["w_uv"], spec.dtype)
+    done, spent = 0, 0.0
+    for b in range(spec.batch):
+        L = int(x["seq_lens"][b])
+        nblk = (L + bs - 1) // bs
+        sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)
+        t0 = time.perf_counter()
+        if spec.append:
+            rows = mla_oracle.cache_rows(synth.as_float(x["h"][b:b + 1], spec.dtype),
+                                         synth.as_float(x["w_dkv"], spec.dtype), synth.as_float(x["w_kr"], spec.dtype),
+                                         x["positions"][b:b + 1], spec.rope_base, spec.dtype)
+            for t, p in enumerate(x["positions"][b]):
+                sub[p // bs, p % bs] = rows[0, t]
+        mla_oracle.decode(qn[b:b + 1], qr[b:b + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :], [L], x["scale"], bs)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    # the sampled sequences are `done` of `batch`; weights are counted in proportion
+    wb = workload_bytes_flops(spec, x["seq_lens"])["bytes"]
+    value = wb * done / spec.batch / spent / 1e9
+    return {"value": round(value, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {spec.batch} sequences (all {spec.n_heads} heads, full context, append included) "
+                      f"in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v2_b64_ctx8192_paged_append")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the hot path here runs on a single MI355X and this build has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    from mla_rank_latent_amd import mla, synth
+
+    spec = synth.presets()[args.workload]
+    print(f"[bench] generating {spec.name} (seed {spec.seed})", file=sys.stderr, flush=True)
+    x = synth.make_inputs(spec)
+
+    def dev(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, spec.dtype,
+                 spec.rope_base)
+    pool, bt, lens = dev(x["pool"]), dev(x["block_table"]), dev(x["seq_lens"])
+    w_uk, w_uv = dev(x["w_uk"]), dev(x["w_uv"])
+    qn, qr = dev(x["q_nope"]), dev(x["q_rope"])
+    has_append = spec.append
+    if has_append:
+        h, w_dkv, w_kr, pos = dev(x["h"]), dev(x["w_dkv"]), dev(x["w_kr"]), dev(x["positions"])
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    out = torch.empty(spec.batch, spec.sq, spec.n_heads, spec.d_nope, dtype=tdt, device="cuda")
+    lse = torch.empty(spec.batch, spec.sq, spec.n_heads, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_bytes(d, spec.batch, spec.sq, args.num_splits), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    dec_args = (d, qn, qr, w_uk, w_uv, pool, bt, lens, x["scale"], ws, out)
+
+    def step(ev_a=None, ev_b=None):
+        if has_append:
+            mla.mla_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, stream=stream)
+        mla.mla_decode_prepare(*dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+        if ev_a is not None:
+            ev_a.record(stream)
+        mla.mla_decode_attend(*dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+        if ev_b is not None:
+            ev_b.record(stream)
+        mla.mla_decode_finish(*dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(ev_a[i], ev_b[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_attn = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
+          f"attention {ms_attn * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    wl = workload_bytes_flops(spec, x["seq_lens"])
+    step_s = ms_step * 1e-3
+    gbs = wl["bytes"] / step_s / 1e9
+    tflops = wl["flops"] / step_s / 1e12
+    tok_s = spec.batch * spec.sq / step_s
+    attn_gbs = wl["cache_bytes"] / (ms_attn * 1e-3) / 1e9
+    attn_tflops = wl["attn_flops"] / (ms_attn * 1e-3) / 1e12
+
+    res = {
+        "metric": "MLA decode GB/s + TFLOP/s (% roofline), tokens/s; B=64 ctx=8K 128 heads",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) cache/queries/hidden states, N(0,1/fan_in) weights)",
+        "config": {"workload": spec.name, "batch": spec.batch, "context": int(max(x["seq_lens"])),
+                   "query_tokens": spec.sq, "heads": spec.n_heads, "d_latent": spec.d_latent,
+                   "d_rope": spec.d_rope, "d_nope": spec.d_nope, "d_model": spec.d_model,
+                   "block_size": spec.block_size, "paged": spec.paged, "append": spec.append,
+                   "num_splits": args.num_splits or "auto"},
+        "tflops": round(tflops, 2),
+        "tokens_per_s": round(tok_s, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "step_bytes": wl["bytes"],
+        "step_flops": wl["flops"],
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
+                     "bytes_per_launch": wl["cache_bytes"],
+                     "mfma_tflops": round(attn_tflops, 2),
+                     "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (oracle, ~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -179,6 +179,38 @@ int mla_decode(const mla_dims* dims, const void* q_nope, const void* q_rope,
                void* workspace, size_t workspace_bytes, void* out, float* lse,
                int32_t* status, void* stream);
 
+/*
+ * The three phases of mla_decode, for callers that schedule them separately
+ * (to overlap the first with other work, or to time the attention kernel on
+ * its own).  Same arguments, same checks and same conventions as mla_decode;
+ * calling all three in order on one stream with the same arguments and
+ * workspace is exactly mla_decode.
+ *  - prepare: absorbed latent queries q~_i = W^UK_i^T q^C_i ‖ q^R_i ("DeepSeek-V2
+ *    ... MLA" page §2.2) and the split plan, into the workspace.
+ *  - attend:  scores over [c ‖ k^R], softmax weights and latent weighted sums
+ *    for every token range (§2.2, §3.2), as partial states in the workspace.
+ *  - finish:  log-sum-exp merge of the partial states and out_i = W^UV_i o_lat
+ *    (§2.2 value-side absorption); writes out and lse.
+ */
+int mla_decode_prepare(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                       const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                       const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                       int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
+                       void* workspace, size_t workspace_bytes, void* out, float* lse,
+                       int32_t* status, void* stream);
+int mla_decode_attend(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                      const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                      int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      int32_t* status, void* stream);
+int mla_decode_finish(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                      const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                      int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -180,10 +180,15 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s
   return L.total;
 }
 
-int mla_decode(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
-               const void* cache, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
-               const int32_t* seq_lens, int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
-               void* workspace, size_t workspace_bytes, void* out, float* lse, int32_t* status, void* stream) {
+namespace {
+
+constexpr int kPhasePrepare = 1, kPhaseAttend = 2, kPhaseFinish = 4;
+
+int decode_phases(int phases, const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
+                  const void* w_uv, const void* cache, int32_t num_blocks, const int32_t* block_table,
+                  int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t sq, float softmax_scale,
+                  int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, float* lse, int32_t* status,
+                  void* stream) {
   int rc = check_dims(dims);
   if (rc != MLA_OK) return rc;
   if (!q_nope || !w_uk || !w_uv || !cache || !block_table || !seq_lens || !workspace || !out) return MLA_ERR_NULL_PTR;
@@ -200,21 +205,40 @@ int mla_decode(const mla_dims* dims, const void* q_nope, const void* q_rope, con
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
-  hipError_t e;
+  hipError_t e = hipSuccess;
   if (dims->dtype == MLA_DTYPE_BF16) {
-    e = launch_absorb_bf16(L, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens,
-                           max_blocks, batch, sq, dims->n_heads, ws, status, st);
-    if (e == hipSuccess)
+    if (phases & kPhasePrepare)
+      e = launch_absorb_bf16(L, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens,
+                             max_blocks, batch, sq, dims->n_heads, ws, status, st);
+    if (e == hipSuccess && (phases & kPhaseAttend))
       e = launch_attn_bf16(L, (const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq,
                            dims->n_heads, softmax_scale, ws, status, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && (phases & kPhaseFinish))
       e = launch_merge_upv_bf16(L, (const uint16_t*)w_uv, batch, sq, dims->n_heads, ws, (uint16_t*)out, lse, st);
   } else {
-    e = launch_decode_f32(dims, L, (const float*)q_nope, (const float*)q_rope, (const float*)w_uk, (const float*)w_uv,
-                          (const float*)cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq, softmax_scale,
-                          ws, (float*)out, lse, status, st);
+    e = launch_decode_f32(phases, dims, L, (const float*)q_nope, (const float*)q_rope, (const float*)w_uk,
+                          (const float*)w_uv, (const float*)cache, num_blocks, block_table, max_blocks, seq_lens,
+                          batch, sq, softmax_scale, ws, (float*)out, lse, status, st);
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+}  // namespace
+
+#define MLA_DECODE_ARGS                                                                                          \
+  dims, q_nope, q_rope, w_uk, w_uv, cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq, softmax_scale, \
+      num_splits, workspace, workspace_bytes, out, lse, status, stream
+#define MLA_DECODE_PARAMS                                                                                        \
+  const mla_dims *dims, const void *q_nope, const void *q_rope, const void *w_uk, const void *w_uv,                \
+      const void *cache, int32_t num_blocks, const int32_t *block_table, int32_t max_blocks,                       \
+      const int32_t *seq_lens, int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits, void *workspace, \
+      size_t workspace_bytes, void *out, float *lse, int32_t *status, void *stream
+
+int mla_decode(MLA_DECODE_PARAMS) {
+  return decode_phases(kPhasePrepare | kPhaseAttend | kPhaseFinish, MLA_DECODE_ARGS);
+}
+int mla_decode_prepare(MLA_DECODE_PARAMS) { return decode_phases(kPhasePrepare, MLA_DECODE_ARGS); }
+int mla_decode_attend(MLA_DECODE_PARAMS) { return decode_phases(kPhaseAttend, MLA_DECODE_ARGS); }
+int mla_decode_finish(MLA_DECODE_PARAMS) { return decode_phases(kPhaseFinish, MLA_DECODE_ARGS); }
 
 }  // extern "C"

@@ -306,22 +306,30 @@ __global__ __launch_bounds__(256) void merge_upv_f32_kernel(mla_dims d, const fl
     lse[mh] = den > 0.0f ? (Mx + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
-hipError_t launch_decode_f32(const mla_dims* d, const WsLayout& L, const float* q_nope, const float* q_rope,
-                             const float* w_uk, const float* w_uv, const float* cache, int num_blocks,
-                             const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int sq,
-                             float scale, uint8_t* ws, float* out, float* lse, int32_t* status, hipStream_t st) {
+hipError_t launch_decode_f32(int phases, const mla_dims* d, const WsLayout& L, const float* q_nope,
+                             const float* q_rope, const float* w_uk, const float* w_uv, const float* cache,
+                             int num_blocks, const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
+                             int batch, int sq, float scale, uint8_t* ws, float* out, float* lse, int32_t* status,
+                             hipStream_t st) {
   const int MH = batch * sq * d->n_heads;
-  hipLaunchKernelGGL(absorb_f32_kernel, dim3(MH + 1), dim3(256), 0, st, *d, q_nope, q_rope, w_uk, seq_lens,
-                     max_blocks, batch, sq, ws, L, status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(L.W, L.rows), dim3(256), 0, st, *d, cache, num_blocks, block_table,
-                     max_blocks, seq_lens, batch, sq, scale * 1.4426950408889634f, ws, L, status);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_upv_f32_kernel, dim3(MH), dim3(256), 0, st, *d, w_uv, batch, sq, (const uint8_t*)ws, L,
-                     out, lse);
-  return hipGetLastError();
+  if (phases & 1) {
+    hipLaunchKernelGGL(absorb_f32_kernel, dim3(MH + 1), dim3(256), 0, st, *d, q_nope, q_rope, w_uk, seq_lens,
+                       max_blocks, batch, sq, ws, L, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(L.W, L.rows), dim3(256), 0, st, *d, cache, num_blocks, block_table,
+                       max_blocks, seq_lens, batch, sq, scale * 1.4426950408889634f, ws, L, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 4) {
+    hipLaunchKernelGGL(merge_upv_f32_kernel, dim3(MH), dim3(256), 0, st, *d, w_uv, batch, sq, (const uint8_t*)ws, L,
+                       out, lse);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -78,7 +78,7 @@ hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_bl
                             hipStream_t st);
 hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads,
                                  uint8_t* ws, uint16_t* out, float* lse, hipStream_t st);
-hipError_t launch_decode_f32(const mla_dims* d, const WsLayout& L, const float* q_nope, const float* q_rope,
+hipError_t launch_decode_f32(int phases, const mla_dims* d, const WsLayout& L, const float* q_nope, const float* q_rope,
                              const float* w_uk, const float* w_uv, const float* cache, int num_blocks,
                              const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
                              int batch, int sq, float scale, uint8_t* ws, float* out, float* lse,

@@ -22,7 +22,8 @@ MLA_STATUS_BAD_LENGTH = 0x2
 MLA_STATUS_BAD_POS = 0x4
 
 EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_q_project",
-           "mla_decode_workspace_bytes", "mla_decode")
+           "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
+           "mla_decode_finish")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or python -m mla_rank_latent_amd.build)")
@@ -47,9 +48,10 @@ _lib.mla_q_project.restype = ctypes.c_int
 _lib.mla_q_project.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I, _I, _P]
 _lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I, _I]
-_lib.mla_decode.restype = ctypes.c_int
-_lib.mla_decode.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _I,
-                            _P, ctypes.c_size_t, _P, _P, _P, _P]
+for _name in ("mla_decode", "mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
+                                     ctypes.c_float, _I, _P, ctypes.c_size_t, _P, _P, _P, _P]
 
 
 class MlaError(RuntimeError):
@@ -109,17 +111,44 @@ def mla_q_project(d: MlaDims, h, w_q, w_qr, positions, q_nope, q_rope, stream=No
         batch, sq, _stream(stream)))
 
 
+def _decode_call(fn: str, d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
+                 workspace, out, lse, status, num_splits, stream) -> None:
+    batch, sq = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _check(fn, getattr(_lib, fn)(
+        ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, sq, float(softmax_scale), num_splits,
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse), _ptr(status),
+        _stream(stream)))
+
+
 def mla_decode(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,
                workspace, out, lse=None, status=None, num_splits: int = 0, stream=None) -> None:
     """q_nope [batch, sq, n_heads, d_nope]; q_rope [batch, sq, n_heads, d_rope] (rotated);
     out [batch, sq, n_heads, d_nope] and optional lse [batch, sq, n_heads] float32 written.
     ``workspace`` is a byte tensor of at least mla_decode_workspace_bytes(d, batch, sq, num_splits)."""
-    batch, sq = int(q_nope.shape[0]), int(q_nope.shape[1])
-    _check("mla_decode", _lib.mla_decode(
-        ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
-        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, sq, float(softmax_scale), num_splits,
-        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse), _ptr(status),
-        _stream(stream)))
+    _decode_call("mla_decode", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
+                 workspace, out, lse, status, num_splits, stream)
+
+
+def mla_decode_prepare(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,
+                       workspace, out, lse=None, status=None, num_splits: int = 0, stream=None) -> None:
+    """First phase of mla_decode (absorbed queries and split plan); same arguments."""
+    _decode_call("mla_decode_prepare", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
+                 workspace, out, lse, status, num_splits, stream)
+
+
+def mla_decode_attend(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,
+                      workspace, out, lse=None, status=None, num_splits: int = 0, stream=None) -> None:
+    """Second phase of mla_decode (split-KV latent attention); same arguments."""
+    _decode_call("mla_decode_attend", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
+                 workspace, out, lse, status, num_splits, stream)
+
+
+def mla_decode_finish(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,
+                      workspace, out, lse=None, status=None, num_splits: int = 0, stream=None) -> None:
+    """Third phase of mla_decode (merge and W^UV up-projection); same arguments."""
+    _decode_call("mla_decode_finish", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
+                 workspace, out, lse, status, num_splits, stream)
 
 
 def raw_library() -> ctypes.CDLL:
