@@ -103,6 +103,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the hot path here runs on a single MI355X and this build has no "
@@ -111,6 +113,16 @@ def main() -> int:
 
     import torch
     from mla_rank_latent_amd import mla, synth
+
+    if args.copy_calibration:
+        # a plain copy of known size: 2^30 bytes read and 2^30 bytes written per dispatch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": 1 << 30, "dispatches": 3}), flush=True)
+        return 0
 
     spec = synth.presets()[args.workload]
     print(f"[bench] generating {spec.name} (seed {spec.seed})", file=sys.stderr, flush=True)

@@ -4,39 +4,37 @@
 // §2.2 matrix absorption and §3.2 decoupled RoPE): for every query row
 // (head i, query token s) with absorbed query q_lat = [W^UK_i^T q^C ‖ q^R],
 // the logits z_j = scale * q_lat . [c_j ‖ k^R_j] over one range of cached
-// tokens, an online softmax over them, and the latent weighted sum
-// sum_j p_j c_j.  Every range leaves a partial state (latent sum, reference
-// maximum, weight sum) that the merge kernel combines.
+// tokens, softmax weights against a per-row reference maximum, and the
+// latent weighted sum sum_j p_j c_j.  Every range leaves a partial state
+// (latent sum, reference maximum, weight sum) that the merge kernel combines.
 //
 // Mapping onto the chip.  All heads share one latent stream, so a workgroup
 // takes 128 query rows (all 128 heads at Sq = 1) against the same cache
-// tiles, and the two contractions are dense GEMMs on MFMA:
-//   S^T[32 tok x 32 rows]  = T[32 tok x 576] . Q^T[576 x 32 rows]     (36 MFMA 32x32x16)
-//   O^T[512 x 32 rows]    += C^T[512 x 32 tok] . P^T[32 tok x 32 rows] (32 MFMA 32x32x16)
-// per wave and 32-token stage.  Each of the 4 waves owns 32 rows: its Q
-// (144 VGPRs) and its O accumulator (256 registers) stay in registers for
-// the whole range; the cache tile is read from HBM once per workgroup.
+// tiles, and both contractions are dense GEMMs on MFMA 32x32x16 (the shape
+// one wave can issue at the matrix core's full rate):
+//   S^T[32 tok x 32 rows]  = T[32 tok x 576] . Q^T[576 x 32 rows]     (36 MFMAs)
+//   O^T[512 x 32 rows]    += C^T[512 x 32 tok] . P^T[32 tok x 32 rows] (32 MFMAs)
+// per wave and 32-token stage.  Four waves of 32 rows, one per SIMD: a wave
+// keeps its Q (144 VGPRs) and its O accumulator (256 AGPRs) in registers for
+// the whole range, and every 16-byte LDS operand read feeds a full 32-row
+// MFMA.  The cache tile is read from HBM once per workgroup.
 //  - Tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging)
-//    into a 4-deep ring of 36 KB stages, so three stages are in flight while
-//    one is consumed.
-//  - LDS rows are 1152 B; 16-byte chunk k of token row t sits at chunk
-//    k ^ sw(t), sw(t) = 2(t mod 4) + ((t / 4) mod 2).  With it the S operand
-//    reads (ds_read_b128, 8 tokens x one chunk) and the transposing O
-//    operand reads (ds_read_b64_tr_b16, 4 tokens x 4 features per 16 lanes)
-//    are both bank-conflict free.
-//  - The PV product needs the cache tile with tokens along K; the LDS
-//    transpose read delivers exactly that from the token-major tile, and the
-//    token order it produces matches the order in which the S result already
-//    sits in registers, so P never leaves registers.
-//  - Softmax runs in log2 units against a fixed per-row reference: the row's
-//    maximum over the first 32 tokens of the range.  Scores may exceed it by
-//    up to 16 (p <= 2^16, well inside bf16/fp32 range).  O is never rescaled
-//    in registers (VALU writes to the MFMA accumulators would push them out
-//    of AGPRs and spill); if a score ever beats the reference by more than
-//    16, the workgroup re-runs the range against the largest score seen,
-//    which is exact and, for real logit spreads, never happens.  The partial
-//    is stored un-normalised with its (reference, weight sum); the merge
-//    kernel normalises.
+//    into a 4-deep ring of 36 KB stages, three stages in flight.
+//  - LDS rows are 1152 B.  16-byte chunk k of token row t sits at chunk
+//    k ^ sw(t), sw(t) = 2 (t mod 4) ^ ((t / 4) mod 8) (XOR within groups of 8
+//    chunks).  Measured with the LDS bank-conflict counter on gfx950, this
+//    makes both the score operand reads (ds_read_b128: 32 rows x 2 chunks)
+//    and the transposing PV operand reads (ds_read_b64_tr_b16: 4 rows x 4
+//    feature quads per 16 lanes) conflict free at 256 B/clk.
+//  - The PV product needs the tile with tokens along K; the LDS transpose
+//    read delivers that from the token-major tile, in the token order in
+//    which the S result already sits in registers, so P never leaves them.
+//  - Scores against a fixed per-row reference (the first stage's maximum):
+//    p = 2^(z - ref) <= 2^16 unless a later score beats the reference by
+//    more than 16, in which case the range is re-run against the largest
+//    score seen (exact; for real logit spreads it never happens).  O is never
+//    rescaled in registers, so its accumulators are written only by MFMAs
+//    and stay in AGPRs.
 #include "device_util.h"
 
 namespace mla {
@@ -45,75 +43,53 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyTau = 16.0f;   // p = 2^(z - reference) stays <= 2^16
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+static_assert(kWaves * kRowsPerWave == kRowsWG, "rows per workgroup");
+constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;   // 9 copies of 1 KB per wave and stage
+constexpr int kPfS = 4;   // score operands read ahead
+constexpr int kPfO = 3;   // PV operands read ahead
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+#define MLA_CONST __attribute__((address_space(4)))
+// Read-only tables go through the constant address space so that wave-uniform
+// lookups become scalar loads (counted by lgkmcnt, never waiting on the
+// in-flight tile copies, which are counted by vmcnt).
+template <typename T>
+__device__ __forceinline__ const MLA_CONST T* as_const(const T* p) {
+  return (const MLA_CONST T*)p;
+}
+
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
 
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ u32x4 lds_read16(const MLA_LDS uint8_t* p) {
-  return *(const MLA_LDS u32x4*)p;
-}
+__device__ __forceinline__ u32x4 lds_read16(const MLA_LDS uint8_t* p) { return *(const MLA_LDS u32x4*)p; }
 
 __device__ __forceinline__ u32x2 lds_read_tr(const MLA_LDS uint8_t* p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Read-only tables are read through the constant address space so that
-// wave-uniform lookups become scalar loads (counted by lgkmcnt, not vmcnt,
-// and so never waiting on the in-flight tile copies).
-#define MLA_CONST __attribute__((address_space(4)))
-template <typename T>
-__device__ __forceinline__ const MLA_CONST T* as_const(const T* p) {
-  return (const MLA_CONST T*)p;
+// One 16-byte-per-lane copy HBM -> LDS: global address = base + voff, LDS
+// address = m0 + 16 * lane.  Issued as asm so that the compiler does not
+// treat every later LDS read as aliasing the copy (it would then wait for all
+// copies in flight); the ring protocol waits for exactly the stage it reads.
+__device__ __forceinline__ void copy16_to_lds(uint64_t base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory");
 }
 
-struct Ctx {
-  const uint16_t* cache;
-  const MLA_CONST int32_t* block_table;
-  int max_blocks;
-  int num_blocks;
-  int32_t* status;
-};
-
-// Issue this wave's 9 direct-to-LDS loads for one 32-token stage.
-// Stage chunk P (16 B) = 64 q + lane holds token t = P / 72, physical chunk
-// P % 72, which is logical chunk (P % 72) ^ swz(t) of that token's row.
-__device__ __forceinline__ void issue_stage(const Ctx& cx, MLA_LDS uint8_t* stage, int wave, int lane,
-                                            int b, int tok0, int tlast) {
-  // the 32-token stage lies inside one 64-token block
-  // wave-uniform by construction; readfirstlane lets the compiler see it and use a scalar load
-  const int idx = __builtin_amdgcn_readfirstlane(b * cx.max_blocks + tok0 / kBlk);
-  int blk = cx.block_table[idx];
-  if (blk < 0 || blk >= cx.num_blocks) {
-    if (lane == 0 && cx.status) atomicOr(cx.status, MLA_STATUS_BAD_BLOCK);
-    blk = 0;
-  }
-  const uint8_t* base = (const uint8_t*)cx.cache + ((size_t)blk * kBlk + (tok0 % kBlk)) * (size_t)(kRow * 2);
-  // Recomputed per stage on purpose: hoisted out of the loop these 9 offsets
-  // would be spilled, and reloading a spill waits on the in-flight copies.
-  int lane_o = lane;
-  asm volatile("" : "+v"(lane_o));
-#pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    int q = wave + 4 * k;
-    int P = 64 * q + lane_o;
-    int t = P / kChunksPerRow;
-    int pc = P - t * kChunksPerRow;
-    int c = pc ^ swz(t);
-    int tt = t < tlast ? t : tlast;   // rows past the end re-read the last valid row
-    const uint8_t* src = base + tt * (kRow * 2) + c * 16;
-    // Issued as asm so the compiler does not treat every later LDS read as
-    // aliasing the in-flight copy (it would wait for all of them); the ring
-    // protocol below waits for exactly the stage it reads.
-    uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(stage + q * 1024));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
-  }
+// a wave-uniform 64-bit address, made visibly uniform (scalar registers)
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ cache, int num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ seq_lens, int batch, int sq, int n_heads, int hg, int W, int P,
     float scale_log2, uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
@@ -131,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   // XCD-aware order: block ids that differ by a multiple of 8 share an XCD (and
   // its L2); the G head groups of one token range take ids 8 apart.
   const int G = Lw.G;
-  int bid = blockIdx.x;
+  const int bid = blockIdx.x;
   const int w = (bid / (8 * G)) * 8 + (bid % 8);
   const int g = (bid / 8) % G;
   if (w >= W) return;
@@ -141,6 +117,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   const MLA_CONST int32_t* piece_base = as_const((const int32_t*)(ws + Lw.off_piece));
   const MLA_CONST int32_t* wgseg = as_const((const int32_t*)(ws + Lw.off_wgseg));
   const MLA_CONST int32_t* lens = as_const(seq_lens);
+  const MLA_CONST int32_t* btab = as_const(block_table);
   const uint16_t* q_lat = (const uint16_t*)(ws + Lw.off_qlat);
   float2* part_ml = (float2*)(ws + Lw.off_lse);
   float* part_o = (float*)(ws + Lw.off_o);
@@ -151,30 +128,73 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   if (lo >= total) return;
   const int hi = lo + quota < total ? lo + quota : total;
 
-  Ctx cx{cache, as_const(block_table), max_blocks, num_blocks, status};
-
   // this lane's query row inside the head group
-  const int row = wave * 32 + n;
+  const int row = wave * kRowsPerWave + n;
   const int hl = row / sq;
   const int s_idx = row - hl * sq;
   const int head = g * hg + hl;
   const bool row_ok = hl < hg && head < n_heads;
 
-  // per-lane LDS offsets for the S operand: token n, chunk (2 ks + hh) ^ swz(n)
+  // score operand (A of 32x32x16): lane reads token n, features 16 ks + 8 hh .. +7:
+  // logical chunk 2 ks + hh at physical ((2 ks + hh) & ~7) | ((2 (ks & 3) + hh) ^ swz(n))
   int s_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s_off[j] = n * (kRow * 2) + ((((2 * j) | hh) ^ swz(n)) * 16);
-  // per-lane LDS offsets for the transposing O operand reads:
-  // lane = 16 g16 + 4 e + q reads token (4 hh + e) (+16 hs + 8 r), features 32 fb + 16 (g16 % 2) + 4 q
+  for (int j = 0; j < 4; ++j) s_off[j] = n * (kRow * 2) + (((2 * j + hh) ^ swz(n)) * 16);
+  // PV operand (A of 32x32x16, transposing read): lane 16 g + 4 e + q (hh = g / 2) reads
+  // token 16 hs + 8 r + 4 hh + e, features 32 fb + 16 (g % 2) + 4 q .. +3, i.e. chunk
+  // 4 fb + 2 (g % 2) + q / 2, half q % 2.  swz(token) = 2 e ^ (4 hs + 2 r + hh): the
+  // (4 hs + 2 r) part is applied below as an XOR of 16 (4 hs + 2 r) on the byte offset.
   const int g16 = lane >> 4;
   const int e_ = (lane >> 2) & 3;
   const int q_ = lane & 3;
   int o_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
-    int clow = (4 * par + 2 * (g16 & 1) + (q_ >> 1)) ^ (2 * e_ + hh);
+    const int clow = (4 * par + 2 * (g16 & 1) + (q_ >> 1)) ^ ((2 * e_) ^ hh);
     o_off[par] = (4 * hh + e_) * (kRow * 2) + clow * 16 + 8 * (q_ & 1);
   }
+  // Stage copy plan: copy q (0..35) of a stage moves stage bytes [1024 q, 1024 q + 1024);
+  // wave w issues copies w, w + 4, ... .  Lane l's 16 B land at stage chunk 64 q + l:
+  // token (64 q + l) / 72, physical chunk (64 q + l) % 72, holding logical chunk
+  // (physical ^ swz(token)) of that token.  ld_off = its byte offset inside the 32 rows.
+  uint32_t ld_off2[(kLoadsPerWave + 1) / 2];
+#pragma unroll
+  for (int k = 0; k < 2 * ((kLoadsPerWave + 1) / 2); ++k) {
+    uint32_t o = 0;
+    if (k < kLoadsPerWave) {
+      const int Pc = 64 * (wave + kWaves * k) + lane;
+      const int t = Pc / kChunksPerRow;
+      const int pc = Pc % kChunksPerRow;
+      o = (uint32_t)(t * (kRow * 2) + (pc ^ swz(t)) * 16);
+    }
+    if (k & 1) ld_off2[k >> 1] |= o << 16;
+    else ld_off2[k >> 1] = o;
+  }
+  auto ld_off = [&](int k) { return (k & 1) ? (ld_off2[k >> 1] >> 16) : (ld_off2[k >> 1] & 0xffffu); };
+
+  // Issue this wave's copies of the 32-token stage starting at token tok0 of
+  // sequence b into ring slot `slot`; rows past tlast re-read row tlast (the
+  // last valid token), so every LDS row holds finite cache data.
+  auto issue_stage = [&](int slot, int b, int tok0, int tlast) {
+    const int idx = __builtin_amdgcn_readfirstlane(b * max_blocks + tok0 / kBlk);
+    int blk = btab[idx];
+    if (blk < 0 || blk >= num_blocks) {
+      if (lane == 0 && status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
+      blk = 0;
+    }
+    const uint64_t base =
+        uniform_addr((const uint8_t*)cache + ((size_t)blk * kBlk + (tok0 % kBlk)) * (size_t)(kRow * 2));
+    const uint32_t dst0 = (uint32_t)(uintptr_t)(lds + slot * kStageBytes + wave * 1024);
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) {
+      uint32_t o = ld_off(k);
+      if (tlast < kSubTok - 1) {
+        const int r = (int)(o / (kRow * 2));
+        if (r > tlast) o -= (uint32_t)((r - tlast) * (kRow * 2));
+      }
+      copy16_to_lds(base, o, __builtin_amdgcn_readfirstlane(dst0 + kWaves * 1024 * k));
+    }
+  };
 
   int seg_i = wgseg[w];
   u32x4 qreg[36];
@@ -187,157 +207,171 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     if (s0 >= hi) break;
     const int a = (lo > s0 ? lo : s0) - s0;
     const int e = (hi < s1 ? hi : s1) - s0;
-    if (a >= e) { again = false; continue; }
+    if (a >= e) {
+      again = false;
+      continue;
+    }
     const int b = seg_i;
     const int piece = g * P + piece_base[b] + (w - s0 / quota);
     int L = lens[b];
     {
-      int cap = max_blocks * kBlk;
-      if (L > cap) L = cap;
-      if (L < 0) L = 0;
+      const int cap = max_blocks * kBlk;
+      L = L > cap ? cap : (L < 0 ? 0 : L);
     }
     const int tok_end = e < L ? e : L;
-    // row limit: query s sees tokens j <= L - sq + s
-    const int lim = L - sq + s_idx;
+    const int lim = L - sq + s_idx;   // query s sees tokens j <= L - sq + s
 
     {
-      const uint16_t* qp = q_lat + ((size_t)(b * sq + s_idx) * n_heads + head) * kRow + 8 * hh;
+      const uint16_t* qp = q_lat + ((size_t)(b * sq + s_idx) * n_heads + (row_ok ? head : 0)) * kRow + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row_ok) v = *(const u32x4*)(qp + 16 * ks);
-        qreg[ks] = v;
+        const u32x4 v = *(const u32x4*)(qp + 16 * ks);
+        qreg[ks] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
 
     float m_ref = again ? m_again : kNegInf;   // reference maximum (log2 units) of this lane's row
-    float m_run = m_ref;                        // largest score seen so far
-    float l_sum = 0.0f;                         // this lane's share of the row's sum of p
+    float m_run = m_ref;                       // largest score seen
+    float l_sum = 0.0f;                        // this lane's share of sum_j p_j
+    bool bad = false;                          // a score beat the reference by more than 2^tau
     f32x16 acc_o[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
     const int nsub = tok_end > a ? (tok_end - a + kSubTok - 1) / kSubTok : 0;
-    {
-      // prologue: stages 0..2
+    auto tlast_of = [&](int k) {
+      const int t = tok_end - 1 - (a + k * kSubTok);
+      return t < kSubTok - 1 ? t : kSubTok - 1;
+    };
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        if (k < nsub) {
-          int tok0 = a + k * kSubTok;
-          int tl = tok_end - 1 - tok0;
-          issue_stage(cx, lds + k * kStageBytes, wave, lane, b, tok0, tl < kSubTok - 1 ? tl : kSubTok - 1);
+    for (int k = 0; k < 3; ++k)
+      if (k < nsub) issue_stage(k, b, a + k * kSubTok, tlast_of(k));
+
+    for (int it = 0; it < nsub; ++it) {
+      // this wave's copies of stage `it` must have landed; later stages may stay in flight
+      const int later = (nsub - 1 - it) < 2 ? (nsub - 1 - it) : 2;
+      if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoadsPerWave));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __syncthreads();   // all waves' copies of stage it visible; stage it - 1 fully consumed
+      if (it + 3 < nsub) issue_stage((it + 3) & 3, b, a + (it + 3) * kSubTok, tlast_of(it + 3));
+      const MLA_LDS uint8_t* st = lds + (it & 3) * kStageBytes;
+      const int tok0 = a + it * kSubTok;
+
+      // ---- S^T = T . Q^T (32 tokens x 32 rows), 36 k-steps of 16 features
+      // two independent accumulation chains (even / odd k-steps) keep the matrix core busy
+      f32x16 acc_s, acc_s1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_s[r] = acc_s1[r] = 0.0f;
+      {
+        u32x4 tv[kPfS];
+#pragma unroll
+        for (int k = 0; k < kPfS; ++k) tv[k] = lds_read16(st + s_off[k & 3] + (k >> 2) * 128);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+          const u32x4 t = tv[ks % kPfS];
+          if (ks + kPfS < 36) tv[ks % kPfS] = lds_read16(st + s_off[(ks + kPfS) & 3] + ((ks + kPfS) >> 2) * 128);
+          if (ks & 1) acc_s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(t), as_bf8(qreg[ks]), acc_s1, 0, 0, 0);
+          else acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(t), as_bf8(qreg[ks]), acc_s, 0, 0, 0);
+        }
+        // keep the operand reads kPfS ahead of the MFMAs that consume them
+#pragma unroll
+        for (int k = 0; k < kPfS; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks + kPfS < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
-      for (int it = 0; it < nsub; ++it) {
-        // wait for this wave's loads of stage `it`; later stages may stay in flight
-        if (it + 2 < nsub) __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
-        else if (it + 1 < nsub) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        __syncthreads();   // all waves' loads visible; stage (it - 1) fully consumed
-        if (it + 3 < nsub) {
-          int tok0 = a + (it + 3) * kSubTok;
-          int tl = tok_end - 1 - tok0;
-          issue_stage(cx, lds + ((it + 3) & 3) * kStageBytes, wave, lane, b, tok0, tl < kSubTok - 1 ? tl : kSubTok - 1);
-        }
-        const MLA_LDS uint8_t* st = lds + (it & 3) * kStageBytes;
-        const int tok0 = a + it * kSubTok;
 
-        // ---- S^T = T . Q^T  (tokens x rows)
-        f32x16 acc_s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_s[r] = 0.0f;
-        {
-          // three operand reads in flight ahead of the MFMA chain
-          u32x4 tv[4];
-#pragma unroll
-          for (int k = 0; k < 3; ++k) tv[k] = lds_read16(st + s_off[k & 3] + (k >> 2) * 128);
-#pragma unroll
-          for (int ks = 0; ks < 36; ++ks) {
-            if (ks + 3 < 36) tv[(ks + 3) & 3] = lds_read16(st + s_off[(ks + 3) & 3] + ((ks + 3) >> 2) * 128);
-            acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(tv[ks & 3]), as_bf8(qreg[ks]), acc_s, 0, 0, 0);
-          }
-        }
-
-        // ---- softmax weights of the 32 tokens against the row's reference (log2 units)
+      // ---- softmax weights against the row reference (log2 units).  Lane holds
+      // row n and tokens 8 (r / 4) + 4 hh + r % 4, r = 0..15.
+      uint32_t pk[8];
+      {
         float z[16];
-        float mx = kNegInf;
-        const bool need_mask = tok0 + kSubTok - 1 > L - sq;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = acc_s[r] * scale_log2;
-          if (need_mask) {
-            int tok = tok0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (tok > lim) v = kNegInf;
+        for (int r = 0; r < 16; ++r) z[r] = (acc_s[r] + acc_s1[r]) * scale_log2;
+        if (tok0 + kSubTok - 1 > L - sq) {   // the stage reaches past some row's last visible token
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tok = tok0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            z[r] = tok > lim ? kNegInf : z[r];
           }
-          z[r] = v;
-          mx = fmaxf(mx, v);
         }
+        float mx = z[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, z[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         m_run = fmaxf(m_run, mx);
-        // a row's reference is its first finite stage maximum (nothing is accumulated before it)
-        if (m_ref == kNegInf) m_ref = mx;
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazyTau) != 0ull && lane == 0) s_retry = 1;
+        m_ref = m_ref == kNegInf ? mx : m_ref;   // a row's reference: its first finite stage maximum
+        bad = bad || (mx > m_ref + kLazyTau);
         const float msafe = m_ref == kNegInf ? 0.0f : m_ref;
-        uint32_t pk[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          float p0 = __builtin_amdgcn_exp2f(z[r] - msafe);
-          float p1 = __builtin_amdgcn_exp2f(z[r + 1] - msafe);
-          uint32_t pp = pack_bf2(p0, p1);
-          pk[r >> 1] = pp;
-          l_sum += __uint_as_float(pp << 16) + __uint_as_float(pp & 0xffff0000u);
+          const float p0 = __builtin_amdgcn_exp2f(z[r] - msafe);
+          const float p1 = __builtin_amdgcn_exp2f(z[r + 1] - msafe);
+          l_sum += p0 + p1;
+          pk[r >> 1] = pack_bf2(p0, p1);
         }
+      }
 
-        // ---- O^T += C^T . P^T  (512 latent features x rows), two 16-token k-steps
-        {
-          // 32 MFMAs (16 feature blocks x 2 token halves), operands read 2 ahead
-          u32x4 av[3];
-#define MLA_OPERAND(j)                                                                                 \
-  ({                                                                                                    \
-    const MLA_LDS uint8_t* p0_ = st + o_off[(j) & 1] + (((j) & 15) >> 1) * 128 + (16 * ((j) >> 4)) * (kRow * 2); \
-    u32x2 lo2_ = lds_read_tr(p0_);                                                                      \
-    u32x2 hi2_ = lds_read_tr(p0_ + 8 * (kRow * 2));                                                     \
-    u32x4 v_ = {lo2_[0], lo2_[1], hi2_[0], hi2_[1]};                                                    \
-    v_;                                                                                                 \
-  })
-          av[0] = MLA_OPERAND(0);
-          av[1] = MLA_OPERAND(1);
-          const u32x4 pb0 = {pk[0], pk[1], pk[2], pk[3]};
-          const u32x4 pb1 = {pk[4], pk[5], pk[6], pk[7]};
+      // ---- O^T += C^T . P^T (512 features x 32 rows): 16 feature blocks x 2 token halves
+      {
+        const u32x4 pb0 = {pk[0], pk[1], pk[2], pk[3]};
+        const u32x4 pb1 = {pk[4], pk[5], pk[6], pk[7]};
+        // operand j: feature block fb = j & 15, token half hs = j >> 4; its two reads take
+        // tokens 16 hs + 4 hh + e (r = 0) and 16 hs + 8 + 4 hh + e (r = 1)
+        auto rd = [&](int j) {
+          const int fb = j & 15, hs = j >> 4;
+          const int o0 = (o_off[fb & 1] ^ (16 * (4 * hs))) + (fb >> 1) * 128 + (16 * hs) * (kRow * 2);
+          const int o1 = (o_off[fb & 1] ^ (16 * (4 * hs + 2))) + (fb >> 1) * 128 + (16 * hs + 8) * (kRow * 2);
+          const u32x2 lo2 = lds_read_tr(st + o0);
+          const u32x2 hi2 = lds_read_tr(st + o1);
+          return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        };
+        u32x4 av[kPfO];
 #pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            if (j + 2 < 32) av[(j + 2) % 3] = MLA_OPERAND(j + 2);
-            acc_o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(av[j % 3]), as_bf8(j < 16 ? pb0 : pb1),
-                                                                    acc_o[j & 15], 0, 0, 0);
-          }
-#undef MLA_OPERAND
+        for (int k = 0; k < kPfO; ++k) av[k] = rd(k);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const u32x4 op = av[j % kPfO];
+          if (j + kPfO < 32) av[j % kPfO] = rd(j + kPfO);
+          acc_o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(op), as_bf8(j < 16 ? pb0 : pb1),
+                                                                  acc_o[j & 15], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kPfO; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (j + kPfO < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __syncthreads();   // ring drained and free; every wave's flag write visible
-      const bool retry = s_retry != 0;
-      __syncthreads();   // every wave has read the flag
-      if (retry) {
-        // a score beat the reference by more than 2^tau: run this range again
-        // against the largest score seen (rare; exact either way)
-        if (tid == 0) s_retry = 0;
-        m_again = m_run;
-        again = true;
-        continue;
-      }
+    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0ull && lane == 0) s_retry = 1;
+    __syncthreads();   // ring free for the next range; every wave's flag visible
+    const bool retry = s_retry != 0;
+    __syncthreads();   // every wave has read the flag
+    if (retry) {
+      // a score beat the reference by more than 2^tau: run this range again
+      // against the largest score seen (rare; exact either way)
+      if (tid == 0) s_retry = 0;
+      m_again = m_run;
+      again = true;
+      continue;
     }
     again = false;
 
     // ---- partial state: un-normalised latent sum, reference max and weight sum
     const float l_tot = l_sum + __shfl_xor(l_sum, 32);
-    float* op = part_o + ((size_t)piece * kRowsWG + row) * kLat;
+    float* op = part_o + ((size_t)piece * kRowsWG + row) * kLat + 4 * hh;
 #pragma unroll
     for (int fb = 0; fb < 16; ++fb) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        f32x4 v = {acc_o[fb][4 * rr], acc_o[fb][4 * rr + 1], acc_o[fb][4 * rr + 2], acc_o[fb][4 * rr + 3]};
-        *(f32x4*)(op + fb * 32 + 8 * rr + 4 * hh) = v;
+        const f32x4 v = {acc_o[fb][4 * rr], acc_o[fb][4 * rr + 1], acc_o[fb][4 * rr + 2], acc_o[fb][4 * rr + 3]};
+        *(f32x4*)(op + fb * 32 + 8 * rr) = v;
       }
     }
     if (hh == 0) part_ml[(size_t)piece * kRowsWG + row] = make_float2(m_ref, l_tot);
@@ -348,11 +382,11 @@ hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_bl
                             int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float scale,
                             uint8_t* ws, int32_t* status, hipStream_t st) {
   // grid: W ranges x G head groups, ordered so the groups of a range share an XCD
-  int wpad = (L.W + 7) / 8 * 8;
+  const int wpad = (L.W + 7) / 8 * 8;
   dim3 grid(wpad * L.G);
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(256), 0, st, cache, num_blocks, block_table, max_blocks, seq_lens,
-                     batch, sq, n_heads, L.hg, L.W, L.P, scale_log2, ws, L, status);
+  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(kWaves * 64), 0, st, cache, num_blocks, block_table, max_blocks,
+                     seq_lens, batch, sq, n_heads, L.hg, L.W, L.P, scale_log2, ws, L, status);
   return hipGetLastError();
 }
 
