@@ -48,7 +48,7 @@ constexpr int kRowsPerWave = 32;
 static_assert(kWaves * kRowsPerWave == kRowsWG, "rows per workgroup");
 constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;   // 9 copies of 1 KB per wave and stage
 constexpr int kPfS = 4;   // score operands read ahead
-constexpr int kPfO = 3;   // PV operands read ahead
+constexpr int kPfO = 5;   // PV operands read ahead
 
 #define MLA_CONST __attribute__((address_space(4)))
 // Read-only tables go through the constant address space so that wave-uniform
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ cache, int num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ seq_lens, int batch, int sq, int n_heads, int hg, int W, int P,
     float scale_log2, uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  // the ring, then 1 KB that absorbs the copies of iterations with no stage left to fetch
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + 1024];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
   __shared__ int s_retry;
   if (threadIdx.x == 0) s_retry = 0;
@@ -172,18 +173,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   }
   auto ld_off = [&](int k) { return (k & 1) ? (ld_off2[k >> 1] >> 16) : (ld_off2[k >> 1] & 0xffffu); };
 
-  // Issue this wave's copies of the 32-token stage starting at token tok0 of
-  // sequence b into ring slot `slot`; rows past tlast re-read row tlast (the
-  // last valid token), so every LDS row holds finite cache data.
-  auto issue_stage = [&](int slot, int b, int tok0, int tlast) {
-    const int idx = __builtin_amdgcn_readfirstlane(b * max_blocks + tok0 / kBlk);
-    int blk = btab[idx];
+  // The block-table entry for token tok0 of sequence b: a scalar load whose
+  // value is checked only when the copies are issued, so that its latency can
+  // hide behind a whole stage of work.
+  auto lookup_block = [&](int b, int tok0) {
+    return btab[__builtin_amdgcn_readfirstlane(b * max_blocks + tok0 / kBlk)];
+  };
+  // Global address of the 32-token stage starting at token tok0, inside cache
+  // block blk.  A block id outside the pool is reported and replaced by block 0.
+  auto stage_base = [&](int blk, int tok0) {
     if (blk < 0 || blk >= num_blocks) {
       if (lane == 0 && status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
       blk = 0;
     }
-    const uint64_t base =
-        uniform_addr((const uint8_t*)cache + ((size_t)blk * kBlk + (tok0 % kBlk)) * (size_t)(kRow * 2));
+    return uniform_addr((const uint8_t*)cache + ((size_t)blk * kBlk + (tok0 % kBlk)) * (size_t)(kRow * 2));
+  };
+  // Issue all of this wave's copies of a stage into ring slot `slot` at once;
+  // rows past tlast re-read row tlast (the last valid token), so every LDS row
+  // holds finite cache data.
+  auto issue_stage = [&](int slot, uint64_t base, int tlast) {
     const uint32_t dst0 = (uint32_t)(uintptr_t)(lds + slot * kStageBytes + wave * 1024);
 #pragma unroll
     for (int k = 0; k < kLoadsPerWave; ++k) {
@@ -195,6 +203,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       copy16_to_lds(base, o, __builtin_amdgcn_readfirstlane(dst0 + kWaves * 1024 * k));
     }
   };
+  // Copies that fetch nothing needed: an in-bounds read of the pool's first rows
+  // into the spare kilobyte.  Every iteration issues the same number of copies,
+  // so one fixed wait count finds each stage landed.
+  const uint64_t idle_base = uniform_addr(cache);
+  const uint32_t idle_dst = (uint32_t)(uintptr_t)(lds + kStages * kStageBytes);
 
   int seg_i = wgseg[w];
   u32x4 qreg[36];
@@ -245,17 +258,40 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       return t < kSubTok - 1 ? t : kSubTok - 1;
     };
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-      if (k < nsub) issue_stage(k, b, a + k * kSubTok, tlast_of(k));
+    for (int k = 0; k < 3; ++k) {
+      if (k < nsub) {
+        issue_stage(k, stage_base(lookup_block(b, a + k * kSubTok), a + k * kSubTok), tlast_of(k));
+      } else {
+#pragma unroll
+        for (int c = 0; c < kLoadsPerWave; ++c) copy16_to_lds(idle_base, ld_off(c), idle_dst);
+      }
+    }
+    // block ids are looked up one stage ahead of their copies, so that the
+    // scalar load's latency is hidden behind a whole stage of work
+    int blk_next = 3 < nsub ? lookup_block(b, a + 3 * kSubTok) : 0;
 
     for (int it = 0; it < nsub; ++it) {
-      // this wave's copies of stage `it` must have landed; later stages may stay in flight
-      const int later = (nsub - 1 - it) < 2 ? (nsub - 1 - it) : 2;
-      if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoadsPerWave));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      // This wave's copies of stage it have landed once at most two stages' worth
+      // (issued by the two previous iterations) remain in flight.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoadsPerWave));
       __syncthreads();   // all waves' copies of stage it visible; stage it - 1 fully consumed
-      if (it + 3 < nsub) issue_stage((it + 3) & 3, b, a + (it + 3) * kSubTok, tlast_of(it + 3));
+      // The copies of stage it + 3 ride along the score MFMAs below.  A ragged
+      // stage (a sequence's last) goes out here in full, with its rows clamped.
+      uint64_t nbase = idle_base;
+      uint32_t ndst = idle_dst, nstride = 0;
+      if (it + 3 < nsub) {
+        const int tok = a + (it + 3) * kSubTok;
+        const int tl = tlast_of(it + 3);
+        const uint64_t base = stage_base(blk_next, tok);
+        if (tl == kSubTok - 1) {
+          nbase = base;
+          ndst = (uint32_t)(uintptr_t)(lds + ((it + 3) & 3) * kStageBytes + wave * 1024);
+          nstride = kWaves * 1024;
+        } else {
+          issue_stage((it + 3) & 3, base, tl);
+        }
+      }
+      if (it + 4 < nsub) blk_next = lookup_block(b, a + (it + 4) * kSubTok);
       const MLA_LDS uint8_t* st = lds + (it & 3) * kStageBytes;
       const int tok0 = a + it * kSubTok;
 
@@ -274,6 +310,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
           if (ks + kPfS < 36) tv[ks % kPfS] = lds_read16(st + s_off[(ks + kPfS) & 3] + ((ks + kPfS) >> 2) * 128);
           if (ks & 1) acc_s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(t), as_bf8(qreg[ks]), acc_s1, 0, 0, 0);
           else acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(t), as_bf8(qreg[ks]), acc_s, 0, 0, 0);
+          if ((ks & 3) == 2)
+            copy16_to_lds(nbase, ld_off(ks >> 2), __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
         }
         // keep the operand reads kPfS ahead of the MFMAs that consume them
 #pragma unroll
