@@ -10,25 +10,38 @@
 // Attention (MLA) 原理与工程实现" §2.2: sum_j p_j W^UV_i c_j = W^UV_i sum_j p_j c_j)
 // restores the head's output, out_i = W^UV_i o_lat (W^UV_i = rows 128 i ..
 // 128 i + 127 of W^UV, §2.1).
-// One workgroup per (head, 32 query rows): it merges its rows into LDS and
-// runs [32 x 512] . [512 x 128] on MFMA 32x32x16.  The merged latent is split
-// into a bf16 high part and a bf16 remainder (two MFMAs per step), which keeps
-// the product close to fp32 accuracy.
+//
+// One workgroup of eight waves per (head, 32 query rows).
+//  - Merge: sixteen threads per row, each owning 32 of its 512 columns
+//    (16 bytes at 256-byte strides, so the sixteen lanes of a row read whole
+//    256-byte blocks).  Two pieces' loads are in flight per thread and the
+//    piece weights are applied branch-free, so the partial states stream at
+//    memory rate instead of one round trip per piece.
+//  - The merged latent goes to LDS as a bf16 high part and a bf16 remainder
+//    (two MFMAs per step keep the product close to fp32 accuracy).
+//  - Up-projection [32 x 512] . [512 x 128] on MFMA 32x32x16: wave (kh, wc)
+//    takes output columns 32 wc .. 32 wc + 31 over latent half kh, with its
+//    W^UV slice loaded into registers before the merge starts; the two
+//    latent halves are summed through LDS.
 #include "device_util.h"
 
 namespace mla {
 
 namespace {
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+constexpr int kMergeRows = 32;
 }  // namespace
 
-__global__ __launch_bounds__(256) void merge_upv_bf16_kernel(const uint16_t* __restrict__ w_uv, int batch, int sq,
+__global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __restrict__ w_uv, int batch, int sq,
                                                              int n_heads, int hg, int P,
                                                              const uint8_t* __restrict__ ws, WsLayout Lw,
                                                              uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 32 * kLat * 2];   // hi and lo parts, 32 rows each
+  // hi and lo parts of the merged latent (32 rows x 512, swizzled 16-byte
+  // chunks), then the upper latent half's partial products (32 x 128 fp32)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kMergeRows * kLat * 2 + kMergeRows * kNope * 4];
   MLA_LDS uint8_t* s_hi = (MLA_LDS uint8_t*)smem;
-  MLA_LDS uint8_t* s_lo = s_hi + 32 * kLat * 2;
+  MLA_LDS uint8_t* s_lo = s_hi + kMergeRows * kLat * 2;
+  MLA_LDS float* s_red = (MLA_LDS float*)(s_lo + kMergeRows * kLat * 2);
 
   const int M = batch * sq;
   const int h = blockIdx.x % n_heads;
@@ -38,24 +51,26 @@ __global__ __launch_bounds__(256) void merge_upv_bf16_kernel(const uint16_t* __r
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int n = lane & 31;
+  const int kh = wave >> 2;    // latent half of the up-projection
+  const int wc = wave & 3;     // output column block
 
-  // Issue the W^UV_i loads first; they overlap with the merge.
-  // B operand (K = latent c, N = output column d): lane holds W^UV[128 h + 32 wave + n][16 ks + 8 hh .. +7].
-  u32x4 bop[32];
+  // B operand (K = latent, N = output column): lane holds
+  // W^UV[128 h + 32 wc + n][256 kh + 16 ks + 8 hh .. +7], ks = 0..15.
+  u32x4 bop[16];
   {
-    const uint16_t* wp = w_uv + ((size_t)h * kNope + 32 * wave + n) * kLat + 8 * hh;
+    const uint16_t* wp = w_uv + ((size_t)h * kNope + 32 * wc + n) * kLat + 256 * kh + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) bop[ks] = *(const u32x4*)(wp + 16 * ks);
+    for (int ks = 0; ks < 16; ++ks) bop[ks] = *(const u32x4*)(wp + 16 * ks);
   }
 
-  // ---- merge: thread = (row i, 64-column part)
+  // ---- merge: thread = (row i, column lane c16); columns 64 j + 4 c16 .. +3, j = 0..7
   {
-    const int i = tid >> 3;
-    const int cpart = tid & 7;
-    const int m = mb * 32 + i;
-    float acc[64];
+    const int i = tid >> 4;
+    const int c16 = tid & 15;
+    const int m = mb * kMergeRows + i;
+    f32x4 acc[8];
 #pragma unroll
-    for (int c = 0; c < 64; ++c) acc[c] = 0.0f;
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float den = 0.0f, Mx = -__builtin_inff();
     if (m < M) {
       const int b = m / sq;
@@ -68,76 +83,89 @@ __global__ __launch_bounds__(256) void merge_upv_bf16_kernel(const uint16_t* __r
       const int p0 = g * P + piece_base[b];
       const int p1 = g * P + piece_base[b + 1];
       for (int p = p0; p < p1; ++p) {
-        float2 ml = part_ml[(size_t)p * Lw.rows + r];
+        const float2 ml = part_ml[(size_t)p * Lw.rows + r];
         if (ml.y > 0.0f) Mx = fmaxf(Mx, ml.x);
       }
-      for (int p = p0; p < p1; ++p) {
-        float2 ml = part_ml[(size_t)p * Lw.rows + r];
-        if (!(ml.y > 0.0f)) continue;
-        const float wk = __builtin_amdgcn_exp2f(ml.x - Mx);
-        den += wk * ml.y;
-        const f32x4* op = (const f32x4*)(part_o + ((size_t)p * Lw.rows + r) * kLat + cpart * 64);
+      if (Mx != -__builtin_inff()) {
+        for (int p = p0; p < p1; p += 2) {
+          // the second piece of the pair; past the end it re-reads piece p with weight 0
+          const int q = p + 1 < p1 ? p + 1 : p;
+          const float2 ml0 = part_ml[(size_t)p * Lw.rows + r];
+          const float2 ml1 = part_ml[(size_t)q * Lw.rows + r];
+          const f32x4* o0 = (const f32x4*)(part_o + ((size_t)p * Lw.rows + r) * kLat) + c16;
+          const f32x4* o1 = (const f32x4*)(part_o + ((size_t)q * Lw.rows + r) * kLat) + c16;
+          f32x4 v0[8], v1[8];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          f32x4 v = op[j];
-          acc[4 * j] += wk * v[0];
-          acc[4 * j + 1] += wk * v[1];
-          acc[4 * j + 2] += wk * v[2];
-          acc[4 * j + 3] += wk * v[3];
+          for (int j = 0; j < 8; ++j) v0[j] = o0[16 * j];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v1[j] = o1[16 * j];
+          // an empty piece has l = 0, m = -inf and O = 0: weight 0
+          const float w0 = ml0.y > 0.0f ? __builtin_amdgcn_exp2f(ml0.x - Mx) : 0.0f;
+          const float w1 = (q != p && ml1.y > 0.0f) ? __builtin_amdgcn_exp2f(ml1.x - Mx) : 0.0f;
+          den += w0 * ml0.y + w1 * ml1.y;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] += w0 * v0[j] + w1 * v1[j];
         }
       }
-      if (cpart == 0 && lse != nullptr)
+      if (c16 == 0 && lse != nullptr)
         lse[(size_t)m * n_heads + h] =
             den > 0.0f ? (Mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    // write 8 chunks of 8 columns, chunk k of row i at k ^ (i % 8); start at a
-    // lane-dependent chunk so the 8 threads of a row hit different banks
+    // columns 64 j + 4 c16 .. +3 are half (c16 & 1) of logical chunk 8 j + c16 / 2,
+    // stored at chunk 8 j + ((c16 / 2) ^ (i % 8))
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = (jj + cpart) & 7;
-      u32x4 vh, vl;
+    for (int j = 0; j < 8; ++j) {
+      u32x2 vh, vl;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x0 = acc[8 * j + 2 * e] * inv, x1 = acc[8 * j + 2 * e + 1] * inv;
-        uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
-        vh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        vl[e] = pack_bf2(x0 - bf2f(h0), x1 - bf2f(h1));
+      for (int e = 0; e < 2; ++e) {
+        const float x0 = acc[j][2 * e] * inv, x1 = acc[j][2 * e + 1] * inv;
+        const uint32_t hp = pack_bf2(x0, x1);
+        vh[e] = hp;
+        vl[e] = pack_bf2(x0 - bf2f((uint16_t)(hp & 0xffffu)), x1 - bf2f((uint16_t)(hp >> 16)));
       }
-      const int chunk = cpart * 8 + j;
-      const int off = i * (kLat * 2) + ((chunk & ~7) | ((chunk & 7) ^ (i & 7))) * 16;
-      *(MLA_LDS u32x4*)(s_hi + off) = vh;
-      *(MLA_LDS u32x4*)(s_lo + off) = vl;
+      const int off = i * (kLat * 2) + (8 * j + ((c16 >> 1) ^ (i & 7))) * 16 + 8 * (c16 & 1);
+      *(MLA_LDS u32x2*)(s_hi + off) = vh;
+      *(MLA_LDS u32x2*)(s_lo + off) = vl;
     }
   }
   __syncthreads();
 
-  // ---- out[32 rows x 32 cols of this wave] = o_lat . W^UV_i^T
+  // ---- out[32 rows x 32 cols of this wave] over latent half kh
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) {
-    const int chunk = 2 * ks + hh;
+  for (int ks = 0; ks < 16; ++ks) {
+    const int chunk = 32 * kh + 2 * ks + hh;
     const int off = n * (kLat * 2) + ((chunk & ~7) | ((chunk & 7) ^ (n & 7))) * 16;
-    u32x4 ah = *(const MLA_LDS u32x4*)(s_hi + off);
-    u32x4 al = *(const MLA_LDS u32x4*)(s_lo + off);
+    const u32x4 ah = *(const MLA_LDS u32x4*)(s_hi + off);
+    const u32x4 al = *(const MLA_LDS u32x4*)(s_lo + off);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ah), as_bf8(bop[ks]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(al), as_bf8(bop[ks]), acc, 0, 0, 0);
   }
-  const int d = 32 * wave + n;
+  // D layout: register r holds row 8 (r / 4) + 4 hh + r % 4, column n
+  if (kh == 1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = mb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-    if (m < M) out[((size_t)m * n_heads + h) * kNope + d] = f2bf(acc[r]);
+    for (int r = 0; r < 16; ++r) s_red[(8 * (r >> 2) + 4 * hh + (r & 3)) * kNope + 32 * wc + n] = acc[r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const int d = 32 * wc + n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int m = mb * kMergeRows + row;
+      if (m < M) out[((size_t)m * n_heads + h) * kNope + d] = f2bf(acc[r] + s_red[row * kNope + d]);
+    }
   }
 }
 
 hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads, uint8_t* ws,
                                  uint16_t* out, float* lse, hipStream_t st) {
   const int M = batch * sq;
-  dim3 grid(n_heads * ((M + 31) / 32));
-  hipLaunchKernelGGL(merge_upv_bf16_kernel, grid, dim3(256), 0, st, w_uv, batch, sq, n_heads, L.hg, L.P,
+  dim3 grid(n_heads * ((M + kMergeRows - 1) / kMergeRows));
+  hipLaunchKernelGGL(merge_upv_bf16_kernel, grid, dim3(512), 0, st, w_uv, batch, sq, n_heads, L.hg, L.P,
                      (const uint8_t*)ws, L, out, lse);
   return hipGetLastError();
 }
