@@ -17,13 +17,38 @@ the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_b64_ctx8192_hbm_traffic.md")
+ATTN_SOURCES = ("mla_rank_latent_amd/csrc/attn_bf16.hip", "mla_rank_latent_amd/csrc/device_util.h",
+                "mla_rank_latent_amd/csrc/mla_internal.h")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter profile, or None when the profile is for
+    another workload or the attention sources changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- ([a-z0-9_]+): (\S+)$", text, flags=re.M))
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if fields.get("workload") != workload or fields.get("attention_sources_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def workload_bytes_flops(spec, seq_lens):
@@ -104,7 +129,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (to calibrate HBM byte counters)")
+                    help="only run a plain 1 GiB streaming kernel (to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the hot path here runs on a single MI355X and this build has no "
@@ -115,11 +140,12 @@ def main() -> int:
     from mla_rank_latent_amd import mla, synth
 
     if args.copy_calibration:
-        # a plain copy of known size: 2^30 bytes read and 2^30 bytes written per dispatch
+        # a plain streaming kernel of known size (dst = src * 1 over 2^28 floats): it reads 2^30 bytes and
+        # writes 2^30 bytes per dispatch; a device-to-device copy_ may run on a DMA engine instead
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_dispatch": 1 << 30, "dispatches": 3}), flush=True)
         return 0
@@ -150,16 +176,23 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     dec_args = (d, qn, qr, w_uk, w_uv, pool, bt, lens, x["scale"], ws, out)
 
+    # arguments marshalled once, so that a step costs the host four foreign calls
+    launches = []
+    if has_append:
+        launches.append(mla.prepared_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, stream=stream))
+    phase = {name: mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+             for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish")}
+
     def step(ev_a=None, ev_b=None):
-        if has_append:
-            mla.mla_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, stream=stream)
-        mla.mla_decode_prepare(*dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+        for launch in launches:
+            launch()
+        phase["mla_decode_prepare"]()
         if ev_a is not None:
             ev_a.record(stream)
-        mla.mla_decode_attend(*dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+        phase["mla_decode_attend"]()
         if ev_b is not None:
             ev_b.record(stream)
-        mla.mla_decode_finish(*dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+        phase["mla_decode_finish"]()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -177,12 +210,14 @@ def main() -> int:
     for i in range(args.steps):
         step(ev_a[i], ev_b[i])
     t_end.record(stream)
+    enqueued = time.perf_counter() - wall0     # host time to issue the steps (well under the GPU time)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
     ms_attn = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / args.steps
     print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
-          f"attention {ms_attn * 1e3:.1f} us", file=sys.stderr, flush=True)
+          f"attention {ms_attn * 1e3:.1f} us; host issue {enqueued / args.steps * 1e6:.1f} us/step", file=sys.stderr,
+          flush=True)
 
     wl = workload_bytes_flops(spec, x["seq_lens"])
     step_s = ms_step * 1e-3
@@ -217,7 +252,7 @@ def main() -> int:
         "step_bytes": wl["bytes"],
         "step_flops": wl["flops"],
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(spec.name),
                      "kernel": "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
                      "bytes_per_launch": wl["cache_bytes"],
                      "mfma_tflops": round(attn_tflops, 2),

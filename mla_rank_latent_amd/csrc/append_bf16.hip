@@ -5,10 +5,12 @@
 // directly and never compressed) and §3.3 (only [c ‖ k^R] is cached):
 //   row = [W^DKV h ‖ RoPE_p(W^KR h)],  written to slot block_table[p / 64] * 64 + p % 64.
 // The 576 output columns and the new tokens form a GEMM [tokens x d] . [d x 576]
-// run on MFMA 16x16x32: one workgroup per (16 tokens, 16 columns), its four
-// waves splitting d and summing their partial tiles in a fixed order (so the
-// result does not depend on timing).  Both operands are K-contiguous in
-// memory (h rows and W rows), so they stream straight from global memory.
+// run on MFMA 16x16x32: one workgroup per (16 tokens, 16 columns), its sixteen
+// waves splitting d (each issues all of its loads before its MFMAs, so the
+// weights stream at memory rate) and summing their partial tiles in a fixed
+// order (so the result does not depend on timing).  Both operands are
+// K-contiguous in memory (h rows and W rows), so they stream straight from
+// global memory.
 // RoPE pairs (x_{2i}, x_{2i+1}) turn by angle p * base^(-2i/64), with the angle,
 // its sine and cosine and the rotation in fp64; each value is then rounded
 // once to bf16.
@@ -18,7 +20,7 @@ namespace mla {
 
 namespace {
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-constexpr int kAppendWaves = 4;
+constexpr int kAppendWaves = 16;
 }  // namespace
 
 __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
@@ -40,15 +42,23 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
   const uint16_t* hrow = h + (size_t)(tok_a < tokens ? tok_a : 0) * d_model;
   const int koff = 8 * (lane >> 4);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int nks = d_model / 32;   // k-steps of 32; wave w takes steps w, w + 4, ...
+  const int nks = d_model / 32;   // k-steps of 32; wave w takes steps w, w + 16, ...
   const int nmine = (nks - wave + kAppendWaves - 1) / kAppendWaves;
-#pragma unroll 8
-  for (int i = 0; i < nmine; ++i) {
-    const int ks = wave + kAppendWaves * i;
-    u32x4 a = *(const u32x4*)(hrow + 32 * ks + koff);
-    u32x4 b = *(const u32x4*)(wrow + 32 * ks + koff);
-    if (tok_a >= tokens) a = u32x4{0u, 0u, 0u, 0u};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), acc, 0, 0, 0);
+  const bool tok_ok = tok_a < tokens;
+  for (int i0 = 0; i0 < nmine; i0 += 8) {
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ks = wave + kAppendWaves * (i0 + u < nmine ? i0 + u : i0);
+      a[u] = *(const u32x4*)(hrow + 32 * ks + koff);
+      b[u] = *(const u32x4*)(wrow + 32 * ks + koff);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // steps past this wave's share repeat an earlier step with a zero operand
+      const u32x4 av = (tok_ok && i0 + u < nmine) ? a[u] : u32x4{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), as_bf8(b[u]), acc, 0, 0, 0);
+    }
   }
   // D: lane holds column lane%16, rows 4 (lane/16) + r
 #pragma unroll

@@ -151,6 +151,43 @@ def mla_decode_finish(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table
                  workspace, out, lse, status, num_splits, stream)
 
 
+def prepared_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, status=None, stream=None):
+    """Marshal mla_cache_append's arguments once and return a zero-argument callable that launches it.
+    For loops that reuse the same buffers: the per-call cost is one foreign call.  The callable keeps
+    references to the tensors, so their memory stays valid while it lives."""
+    fn = _lib.mla_cache_append
+    keep = (d, h, w_dkv, w_kr, positions, block_table, cache, status)
+    args = (ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(positions), _ptr(block_table),
+            int(block_table.shape[1]), _ptr(cache), int(cache.shape[0]), int(h.shape[0]), int(h.shape[1]),
+            _ptr(status), _stream(stream))
+
+    def launch(_keep=keep):
+        rc = fn(*args)
+        if rc != 0:
+            raise MlaError("mla_cache_append", rc)
+    return launch
+
+
+def prepared_decode(fn_name: str, d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens,
+                    softmax_scale: float, workspace, out, lse=None, status=None, num_splits: int = 0, stream=None):
+    """Marshal the arguments of ``fn_name`` (mla_decode or one of its phases) once and return a
+    zero-argument callable that launches it; see prepared_cache_append."""
+    if fn_name not in ("mla_decode", "mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
+        raise ValueError(fn_name)
+    fn = getattr(_lib, fn_name)
+    keep = (d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, workspace, out, lse, status)
+    args = (ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
+            _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(q_nope.shape[0]), int(q_nope.shape[1]),
+            float(softmax_scale), num_splits, _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+            _ptr(out), _ptr(lse), _ptr(status), _stream(stream))
+
+    def launch(_keep=keep):
+        rc = fn(*args)
+        if rc != 0:
+            raise MlaError(fn_name, rc)
+    return launch
+
+
 def raw_library() -> ctypes.CDLL:
     """The loaded shared library (tests call its entry points directly)."""
     return _lib

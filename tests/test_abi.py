@@ -105,3 +105,47 @@ def test_append_and_qproj_argument_errors():
     q2 = list(q)
     q2[6] = 0
     assert lib.mla_q_project(ctypes.byref(v2), *q2) == -2
+
+
+class _FakeTensor:
+    """Just enough of a tensor for the prepared launchers: a device address and a shape."""
+
+    def __init__(self, addr, shape, itemsize=2):
+        self.addr, self.shape, self.itemsize = addr, shape, itemsize
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        return self.itemsize
+
+
+def test_prepared_launchers_check_on_every_call():
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    T = _FakeTensor
+    q = T(FAKE, (2, 1, 128, 128))
+    qr = T(FAKE, (2, 1, 128, 64))
+    cache = T(FAKE, (16, 64, 576))
+    bt = T(FAKE, (2, 8), 4)
+    lens = T(FAKE, (2,), 4)
+    ws = T(FAKE, (1024,), 1)            # far too small: the library refuses before launching
+    out = T(FAKE, (2, 1, 128, 128))
+    with pytest.raises(ValueError):
+        mla.prepared_decode("mla_decode_everything", v2, q, qr, q, q, cache, bt, lens, 0.07, ws, out, stream=0)
+    for fn in ("mla_decode", "mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
+        launch = mla.prepared_decode(fn, v2, q, qr, q, q, cache, bt, lens, 0.07, ws, out, num_splits=4, stream=0)
+        for _ in range(2):
+            with pytest.raises(mla.MlaError) as err:
+                launch()
+            assert err.value.code == -5
+    h = T(FAKE, (2, 0, 5120))           # no tokens: rejected as bad dims
+    append = mla.prepared_cache_append(v2, h, q, q, bt, bt, cache, stream=0)
+    with pytest.raises(mla.MlaError) as err:
+        append()
+    assert err.value.code == -2
