@@ -179,7 +179,10 @@ def main() -> int:
     # arguments marshalled once, so that a step costs the host four foreign calls
     launches = []
     if has_append:
-        launches.append(mla.prepared_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, stream=stream))
+        n_ws = mla.mla_cache_append_workspace_bytes(d, int(h.shape[0]), int(h.shape[1]))
+        append_ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws else None
+        launches.append(mla.prepared_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, workspace=append_ws,
+                                                  stream=stream))
     phase = {name: mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
              for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish")}
 

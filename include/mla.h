@@ -115,13 +115,27 @@ size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens);
  * positions  [batch, t]                     int32 (device)
  * block_table[batch, max_blocks]            int32 (device)
  * cache      [num_blocks, block_size, d_latent + d_rope]  dtype, written in place
+ * workspace  optional device scratch of mla_cache_append_workspace_bytes(dims,
+ *            batch, t) bytes, 16-byte aligned, contents irrelevant and clobbered.
+ *            With it (bf16) the products are split over the d_model axis across
+ *            many workgroups and summed in a fixed order by a second kernel, so
+ *            the weights stream at memory rate; NULL (with workspace_bytes 0)
+ *            runs one kernel that needs no scratch.  Either way the result does
+ *            not depend on timing; the two paths may differ in the last bit,
+ *            because they sum in different orders.
  * status     optional int32 (device), OR-ed with MLA_STATUS_BAD_POS/BAD_BLOCK; a
  *            row whose position or block is invalid is skipped.
  */
 int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr,
                      const int32_t* positions, const int32_t* block_table, int32_t max_blocks,
                      void* cache, int32_t num_blocks, int32_t batch, int32_t t,
-                     int32_t* status, void* stream);
+                     void* workspace, size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * Workspace bytes for mla_cache_append's split path with this batch shape, or
+ * 0 when the path needs none (fp32) or the arguments are invalid.
+ */
+size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t t);
 
 /*
  * Project the query hidden states of `sq` tokens per sequence:

@@ -134,9 +134,15 @@ size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens) {
   return (size_t)tokens * ((size_t)dims->d_latent + dims->d_rope) * elem_size(dims->dtype);
 }
 
+size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t t) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || t < 1 || (long long)batch * t >= (1ll << 30)) return 0;
+  if (dims->dtype != MLA_DTYPE_BF16) return 0;
+  return append_split_ws_bytes(dims->d_model, (long long)batch * t);
+}
+
 int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr, const int32_t* positions,
                      const int32_t* block_table, int32_t max_blocks, void* cache, int32_t num_blocks, int32_t batch,
-                     int32_t t, int32_t* status, void* stream) {
+                     int32_t t, void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
   int rc = check_dims(dims);
   if (rc != MLA_OK) return rc;
   if (!h || !w_dkv || !w_kr || !positions || !block_table || !cache) return MLA_ERR_NULL_PTR;
@@ -144,11 +150,18 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
   if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
   if ((long long)batch * t >= (1ll << 30)) return MLA_ERR_CAPACITY;
   if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(positions) || !aligned16(block_table) ||
-      !aligned16(cache) || (status && ((uintptr_t)status & 3u)))
+      !aligned16(cache) || (status && ((uintptr_t)status & 3u)) || (workspace && !aligned16(workspace)))
     return MLA_ERR_BAD_ALIGN;
+  const bool split = workspace != nullptr && dims->dtype == MLA_DTYPE_BF16;
+  if (split && workspace_bytes < append_split_ws_bytes(dims->d_model, (long long)batch * t))
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (dims->dtype == MLA_DTYPE_BF16)
+  if (split)
+    e = launch_append_split_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions,
+                                 block_table, max_blocks, (uint16_t*)cache, num_blocks, batch * t, t, dims->d_model,
+                                 dims->rope_base, (float*)workspace, status, st);
+  else if (dims->dtype == MLA_DTYPE_BF16)
     e = launch_append_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions, block_table,
                            max_blocks, (uint16_t*)cache, num_blocks, batch * t, t, dims->d_model, dims->rope_base,
                            status, st);

@@ -105,6 +105,163 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split path (a caller workspace is given).  Every weight row is fetched once
+// per 64 tokens: workgroup (32-column tile, 64-token group, K slice) computes
+// its [64 x 32] partial product over a slice of at most kSliceSteps k-steps of
+// d_model and stores it in fp32.  The slice's 96 row pieces (64 tokens of h,
+// 32 weight rows) are first copied to LDS with direct-to-LDS loads, each of
+// which reads 1 KB of contiguous memory (reading the MFMA operands straight
+// from global memory touches 16 rows 10 KB apart per instruction, which the L1
+// serves poorly).  LDS rows are padded to an odd number of 16-byte chunks, so
+// the 16 rows of an operand read fall in distinct banks.  A second kernel sums
+// the slices of each element in slice order (so the result does not depend on
+// timing), applies RoPE to the k^R pairs and writes the bf16 rows.
+// Workspace layout: [token][slice][576] fp32.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kSliceSteps = 10;                    // k-steps (32 elements) per K slice, at most
+constexpr int kSliceChunks = 4 * kSliceSteps + 1;  // 16-byte chunks per padded LDS row
+constexpr int kTileRows = 64 + 32;                 // tokens + weight rows of one tile
+}  // namespace
+
+__global__ __launch_bounds__(256) void append_partial_bf16_kernel(const uint16_t* __restrict__ h,
+                                                                  const uint16_t* __restrict__ w_dkv,
+                                                                  const uint16_t* __restrict__ w_kr, int tokens,
+                                                                  int d_model, int nslice, float* __restrict__ part) {
+  // whole 1 KB copies: the lanes of the last copy past the tile still write their 16 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(kTileRows * kSliceChunks + 63) / 64 * 1024];
+  MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
+  const int ct = blockIdx.x;   // 32-column tile of the 576-wide row
+  const int tg = blockIdx.y;   // 64-token group
+  const int sl = blockIdx.z;   // K slice
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nks = d_model / 32;
+  const int k0 = (int)((long long)sl * nks / nslice), k1 = (int)((long long)(sl + 1) * nks / nslice);
+  const int nsteps = k1 - k0;                       // 1 .. kSliceSteps
+  const int rch = 4 * nsteps + 1;                   // chunks per padded LDS row (odd)
+
+  // copy: LDS chunk P = 64 q + lane holds row P / rch, chunk P % rch (the last chunk of a
+  // row is padding: it re-reads the row's first chunk)
+  const int nchunks = kTileRows * rch;
+  for (int q = wave; q * 64 < nchunks; q += 4) {
+    int P = q * 64 + lane;
+    if (P >= nchunks) P = nchunks - 1;              // the tail lanes repeat the last chunk
+    const int row = P / rch;
+    int ch = P - row * rch;
+    if (ch == rch - 1) ch = 0;
+    const uint16_t* src;
+    if (row < 64) {
+      const int tok = tg * 64 + row;
+      src = h + (size_t)(tok < tokens ? tok : 0) * d_model;
+    } else {
+      const int col = ct * 32 + (row - 64);
+      src = col < kLat ? w_dkv + (size_t)col * d_model : w_kr + (size_t)(col - kLat) * d_model;
+    }
+    src += 32 * k0 + 8 * ch;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + q * 1024));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  // wave w: tokens 16 w .. +15 (A rows) against the 32 columns (two 16-wide B blocks)
+  const bool tok_ok = tg * 64 + wave * 16 + (lane & 15) < tokens;
+  const MLA_LDS uint8_t* arow = lds + (wave * 16 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
+  const MLA_LDS uint8_t* brow0 = lds + (64 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
+  const MLA_LDS uint8_t* brow1 = brow0 + 16 * rch * 16;
+  f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int ks = 0; ks < nsteps; ++ks) {
+    u32x4 a = *(const MLA_LDS u32x4*)(arow + 64 * ks);
+    const u32x4 b0 = *(const MLA_LDS u32x4*)(brow0 + 64 * ks);
+    const u32x4 b1 = *(const MLA_LDS u32x4*)(brow1 + 64 * ks);
+    if (!tok_ok) a = u32x4{0u, 0u, 0u, 0u};
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b0), acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b1), acc[1], 0, 0, 0);
+  }
+  // D: lane holds column lane % 16 of its 16-column block, tokens 4 (lane / 16) + r of the wave's 16
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tg * 64 + wave * 16 + 4 * (lane >> 4) + r;
+      if (t < tokens) part[((size_t)t * nslice + sl) * kRow + ct * 32 + nb * 16 + (lane & 15)] = acc[nb][r];
+    }
+}
+
+__global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __restrict__ part, int nslice,
+                                                                 const int32_t* __restrict__ positions,
+                                                                 const int32_t* __restrict__ block_table,
+                                                                 int max_blocks, uint16_t* __restrict__ cache,
+                                                                 int num_blocks, int tokens, int t_per_seq,
+                                                                 double rope_base, int32_t* status) {
+  // thread = (token, pair of adjacent columns): a RoPE pair for the k^R part
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)tokens * (kRow / 2)) return;
+  const int tok = (int)(idx / (kRow / 2));
+  const int col = 2 * (int)(idx % (kRow / 2));
+  const float* pp = part + (size_t)tok * nslice * kRow + col;
+  float v0 = 0.0f, v1 = 0.0f;
+  for (int s0 = 0; s0 < nslice; s0 += 8) {
+    float2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = *(const float2*)(pp + (size_t)(s0 + u < nslice ? s0 + u : s0) * kRow);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < nslice) {
+        v0 += p[u].x;
+        v1 += p[u].y;
+      }
+  }
+  const int b = tok / t_per_seq;
+  const int pos = positions[tok];
+  if (pos < 0 || pos >= max_blocks * kBlk) {
+    if (status) atomicOr(status, MLA_STATUS_BAD_POS);
+    return;
+  }
+  const int blk = block_table[(size_t)b * max_blocks + pos / kBlk];
+  if (blk < 0 || blk >= num_blocks) {
+    if (status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
+    return;
+  }
+  uint32_t outv;
+  if (col < kLat) {
+    outv = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+  } else {
+    double y0, y1;
+    rope_pair((double)v0, (double)v1, pos, (col - kLat) >> 1, kRope, rope_base, &y0, &y1);
+    outv = (uint32_t)d2bf(y0) | ((uint32_t)d2bf(y1) << 16);
+  }
+  *(uint32_t*)(cache + ((size_t)blk * kBlk + pos % kBlk) * kRow + col) = outv;
+}
+
+int append_split_slices(int d_model) {
+  const int nks = d_model / 32;
+  return (nks + kSliceSteps - 1) / kSliceSteps;
+}
+
+size_t append_split_ws_bytes(int d_model, long long tokens) {
+  return (size_t)append_split_slices(d_model) * (size_t)tokens * kRow * sizeof(float);
+}
+
+hipError_t launch_append_split_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
+                                    const int32_t* positions, const int32_t* block_table, int max_blocks,
+                                    uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
+                                    float rope_base, float* ws, int32_t* status, hipStream_t st) {
+  const int nslice = append_split_slices(d_model);
+  dim3 grid1(kRow / 32, (tokens + 63) / 64, nslice);
+  hipLaunchKernelGGL(append_partial_bf16_kernel, grid1, dim3(256), 0, st, h, w_dkv, w_kr, tokens, d_model, nslice,
+                     ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long items = (long long)tokens * (kRow / 2);
+  dim3 grid2((unsigned)((items + 255) / 256));
+  hipLaunchKernelGGL(append_finish_bf16_kernel, grid2, dim3(256), 0, st, (const float*)ws, nslice, positions,
+                     block_table, max_blocks, cache, num_blocks, tokens, t_per_seq, (double)rope_base, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_append_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr, const int32_t* positions,
                               const int32_t* block_table, int max_blocks, uint16_t* cache, int num_blocks, int tokens,
                               int t_per_seq, int d_model, float rope_base, int32_t* status, hipStream_t st) {

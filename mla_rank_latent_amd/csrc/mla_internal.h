@@ -59,6 +59,13 @@ int device_cu_count();
 // ---------------------------------------------------------------------------
 // Launchers (one per kernel family).  Each returns hipSuccess or the launch error.
 // ---------------------------------------------------------------------------
+// split append: K slices, workspace bytes, launcher (workspace = fp32 partial products)
+int append_split_slices(int d_model);
+size_t append_split_ws_bytes(int d_model, long long tokens);
+hipError_t launch_append_split_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
+                                    const int32_t* positions, const int32_t* block_table, int max_blocks,
+                                    uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
+                                    float rope_base, float* ws, int32_t* status, hipStream_t st);
 hipError_t launch_append_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
                               const int32_t* positions, const int32_t* block_table, int max_blocks,
                               uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,

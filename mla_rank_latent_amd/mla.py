@@ -21,8 +21,8 @@ MLA_STATUS_BAD_BLOCK = 0x1
 MLA_STATUS_BAD_LENGTH = 0x2
 MLA_STATUS_BAD_POS = 0x4
 
-EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_q_project",
-           "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
+EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_append_workspace_bytes",
+           "mla_q_project", "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
            "mla_decode_finish")
 
 if not os.path.exists(LIB_PATH):
@@ -43,7 +43,10 @@ _lib.mla_status_str.argtypes = [ctypes.c_int]
 _lib.mla_cache_bytes.restype = ctypes.c_size_t
 _lib.mla_cache_bytes.argtypes = [ctypes.POINTER(MlaDims), ctypes.c_int64]
 _lib.mla_cache_append.restype = ctypes.c_int
-_lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P]
+_lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, ctypes.c_size_t,
+                                  _P, _P]
+_lib.mla_cache_append_workspace_bytes.restype = ctypes.c_size_t
+_lib.mla_cache_append_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I]
 _lib.mla_q_project.restype = ctypes.c_int
 _lib.mla_q_project.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I, _I, _P]
 _lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -94,13 +97,24 @@ def mla_decode_workspace_bytes(d: MlaDims, batch: int, sq: int, num_splits: int 
     return int(_lib.mla_decode_workspace_bytes(ctypes.byref(d), batch, sq, num_splits))
 
 
-def mla_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, status=None, stream=None) -> None:
+def mla_cache_append_workspace_bytes(d: MlaDims, batch: int, t: int) -> int:
+    return int(_lib.mla_cache_append_workspace_bytes(ctypes.byref(d), batch, t))
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else int(t.numel() * t.element_size())
+
+
+def mla_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, workspace=None, status=None,
+                     stream=None) -> None:
     """h [batch, t, d_model]; positions [batch, t] int32; block_table [batch, max_blocks] int32;
-    cache [num_blocks, block_size, d_latent + d_rope] (written in place)."""
+    cache [num_blocks, block_size, d_latent + d_rope] (written in place); optional ``workspace``, a byte
+    tensor of at least mla_cache_append_workspace_bytes(d, batch, t), selects the split path."""
     batch, t = int(h.shape[0]), int(h.shape[1])
     _check("mla_cache_append", _lib.mla_cache_append(
         ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(positions), _ptr(block_table),
-        int(block_table.shape[1]), _ptr(cache), int(cache.shape[0]), batch, t, _ptr(status), _stream(stream)))
+        int(block_table.shape[1]), _ptr(cache), int(cache.shape[0]), batch, t, _ptr(workspace), _nbytes(workspace),
+        _ptr(status), _stream(stream)))
 
 
 def mla_q_project(d: MlaDims, h, w_q, w_qr, positions, q_nope, q_rope, stream=None) -> None:
@@ -151,15 +165,16 @@ def mla_decode_finish(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table
                  workspace, out, lse, status, num_splits, stream)
 
 
-def prepared_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, status=None, stream=None):
+def prepared_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, workspace=None, status=None,
+                          stream=None):
     """Marshal mla_cache_append's arguments once and return a zero-argument callable that launches it.
     For loops that reuse the same buffers: the per-call cost is one foreign call.  The callable keeps
     references to the tensors, so their memory stays valid while it lives."""
     fn = _lib.mla_cache_append
-    keep = (d, h, w_dkv, w_kr, positions, block_table, cache, status)
+    keep = (d, h, w_dkv, w_kr, positions, block_table, cache, workspace, status)
     args = (ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(positions), _ptr(block_table),
             int(block_table.shape[1]), _ptr(cache), int(cache.shape[0]), int(h.shape[0]), int(h.shape[1]),
-            _ptr(status), _stream(stream))
+            _ptr(workspace), _nbytes(workspace), _ptr(status), _stream(stream))
 
     def launch(_keep=keep):
         rc = fn(*args)

@@ -39,6 +39,7 @@ def mla_dims(spec: synth.Spec):
 
 class GpuCase:
     """Device copies of one generated workload, plus the calls of one decode step."""
+    split_append = True    # append through the workspace (split) path
 
     def __init__(self, x: dict, num_splits: int = 0):
         import torch
@@ -77,10 +78,16 @@ class GpuCase:
         assert nbytes > 0
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
-    def append(self):
+    def append(self, split=True):
+        """split: use the workspace (split over d_model) path; False: the single-kernel path."""
+        import torch
         from mla_rank_latent_amd import mla
+        ws = None
+        if split:
+            n = mla.mla_cache_append_workspace_bytes(self.d, int(self.h.shape[0]), int(self.h.shape[1]))
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda") if n else None
         mla.mla_cache_append(self.d, self.h, self.w_dkv, self.w_kr, self.positions, self.block_table, self.pool,
-                             status=self.status)
+                             workspace=ws, status=self.status)
 
     def q_project(self):
         from mla_rank_latent_amd import mla
@@ -95,7 +102,7 @@ class GpuCase:
     def step(self):
         """One pass of the hot path: append (if the workload has one), project (tiny case), decode."""
         if self.spec.append or self.spec.q_from_hidden:
-            self.append()
+            self.append(self.split_append)
         if self.spec.q_from_hidden:
             self.q_project()
         self.decode()

@@ -91,7 +91,7 @@ def test_decode_argument_errors():
 def test_append_and_qproj_argument_errors():
     lib = mla.raw_library()
     v2 = mla.dims(128, 128, 64, 512, 5120)
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, 2, 1, None, None]
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, 2, 1, None, 0, None, None]
     assert lib.mla_cache_append(ctypes.byref(v2), *args[:4], None, *args[5:]) == -1
     bad_t = list(args)
     bad_t[9] = 0
@@ -100,6 +100,16 @@ def test_append_and_qproj_argument_errors():
     mis[0] = FAKE + 2
     assert lib.mla_cache_append(ctypes.byref(v2), *mis) == -4
     assert lib.mla_cache_append(ctypes.byref(mla.dims(128, 128, 64, 512, 5000)), *args) == -8
+    need = lib.mla_cache_append_workspace_bytes(ctypes.byref(v2), 2, 1)
+    assert need == 16 * 2 * 576 * 4                     # sixteen K slices of fp32 partial rows
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(v2), 0, 1) == 0
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(mla.dims(8, 16, 8, 32, 64, dtype="f32")), 2, 1) == 0
+    ws_small = list(args)
+    ws_small[10], ws_small[11] = FAKE, need - 1
+    assert lib.mla_cache_append(ctypes.byref(v2), *ws_small) == -5
+    ws_mis = list(args)
+    ws_mis[10], ws_mis[11] = FAKE + 8, need
+    assert lib.mla_cache_append(ctypes.byref(v2), *ws_mis) == -4
     q = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, None]
     assert lib.mla_q_project(ctypes.byref(v2), *q[:2], None, *q[3:]) == -1
     q2 = list(q)

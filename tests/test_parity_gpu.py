@@ -39,10 +39,12 @@ def test_tiny_f32_end_to_end():
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 1e-5
 
 
-def _bf16_case(spec, num_splits=0, heads=None):
+def _bf16_case(spec, num_splits=0, heads=None, split_append=True):
     x = synth.make_inputs(spec)
-    H.log(f"{spec.name} seed={spec.seed} B={spec.batch} sq={spec.sq} lens={list(x['seq_lens'])[:8]} splits={num_splits}")
+    H.log(f"{spec.name} seed={spec.seed} B={spec.batch} sq={spec.sq} lens={list(x['seq_lens'])[:8]} splits={num_splits}"
+          f" split_append={split_append}")
     c = H.GpuCase(x, num_splits)
+    c.split_append = split_append
     c.step()
     import torch
     torch.cuda.synchronize()
@@ -64,9 +66,10 @@ def test_bf16_small(name, batch, sq, lens, paged):
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
 
 
-def test_bf16_append_then_decode():
+@pytest.mark.parametrize("split_append", [True, False])
+def test_bf16_append_then_decode(split_append):
     spec = H.small_spec("append_b2", 2, 1, [130, 64], append=True)
-    x, c = _bf16_case(spec)
+    x, c = _bf16_case(spec, split_append=split_append)
     assert int(c.status.item()) == 0
     rows = H.oracle_append_rows(x)
     pool = H.host(c.pool)
@@ -139,7 +142,8 @@ def test_deterministic_and_lse_normalised():
         assert abs(H.lse_probability_sum(x, b, s, h, lse[b, s, h]) - 1.0) <= 1e-2
 
 
-def test_append_dyadic_is_bit_exact():
+@pytest.mark.parametrize("split", [True, False])
+def test_append_dyadic_is_bit_exact(split):
     """On dyadic inputs every partial sum is exact in fp32, so the latent part of
     the appended row equals the oracle's rounded row bit for bit; nothing
     outside the appended rows changes."""
@@ -149,10 +153,10 @@ def test_append_dyadic_is_bit_exact():
     x["h"] = synth.f32_to_bf16_bits(rng.integers(-2, 3, size=x["h"].shape).astype(np.float32))
     x["w_dkv"] = synth.f32_to_bf16_bits((rng.integers(-64, 65, size=x["w_dkv"].shape) / 64.0).astype(np.float32))
     x["w_kr"] = synth.f32_to_bf16_bits((rng.integers(-64, 65, size=x["w_kr"].shape) / 64.0).astype(np.float32))
-    H.log("dyadic_b3 append")
+    H.log(f"dyadic_b3 append split={split}")
     c = H.GpuCase(x)
     before = x["pool"].copy()
-    c.append()
+    c.append(split)
     import torch
     torch.cuda.synchronize()
     assert int(c.status.item()) == 0
@@ -168,3 +172,36 @@ def test_append_dyadic_is_bit_exact():
         kr = synth.bf16_bits_to_f32(after[blk, p % 64, 512:]).astype(np.float64)
         assert np.all(np.abs(kr - rows[b, 0, 512:]) <= H.bf16_ulp(rows[b, 0, 512:]) + 1e-30)
     assert np.array_equal(after[~touched], before[~touched])
+
+
+def test_append_paths_agree():
+    """The split and single-kernel append paths sum in different orders: on N(0,1)
+    data they agree to within one bf16 ulp, and the rest of the pool is untouched
+    by either (65 tokens: a ragged 64-token group)."""
+    import torch
+    spec = H.small_spec("append_paths_b65", 65, 1, [1 + (7 * b) % 200 for b in range(65)], append=True, seed=21)
+    x = synth.make_inputs(spec)
+    pools = []
+    for split in (True, False):
+        H.log(f"append_paths_b65 split={split}")
+        c = H.GpuCase(x)
+        c.append(split)
+        torch.cuda.synchronize()
+        assert int(c.status.item()) == 0
+        pools.append(c.pool.view(torch.int16).cpu().numpy().view(np.uint16))
+    changed = np.any(pools[0] != x["pool"], axis=-1) | np.any(pools[1] != x["pool"], axis=-1)
+    assert changed.sum() <= spec.batch                 # only the appended rows
+    a, b = (synth.bf16_bits_to_f32(p[changed]).astype(np.float64) for p in pools)
+    # latent part: one bf16 ulp of the value, plus what two fp32 summation orders of a
+    # 5120-term dot product can differ by (a few 1e-7 at unit scale; 2^-18 of the
+    # row's rms bounds it), which matters only for values that cancel to near zero
+    d = np.abs(a[:, :512] - b[:, :512])
+    rms = np.sqrt(np.mean(a[:, :512] ** 2, axis=1, keepdims=True))
+    lim = 2.0 ** -7 * np.maximum(np.abs(a[:, :512]), np.abs(b[:, :512])) + 2.0 ** -18 * rms
+    bad = np.argwhere(d > lim)
+    H.log(f"append_paths_b65 latent: {len(bad)} elements over one ulp; worst rel "
+          f"{float(np.max(d / np.maximum(lim * 2.0 ** 7, 1e-30))):.3e}; first {[(int(r), int(k), a[r, k], b[r, k]) for r, k in bad[:4]]}")
+    assert len(bad) == 0
+    # rotary part: a rotation can cancel, so one ulp of the rotated pair's length (plus rounding of each side)
+    pair = np.sqrt(a[:, 512::2] ** 2 + a[:, 513::2] ** 2).repeat(2, axis=1)
+    assert np.all(np.abs(a[:, 512:] - b[:, 512:]) <= 2.0 ** -6 * pair + 1e-30)
