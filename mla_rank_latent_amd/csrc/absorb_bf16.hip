@@ -10,9 +10,13 @@
 // [M x 128] . [128 x 128] on MFMA 32x32x16.  The contraction runs along the
 // rows of W^UK (d_h), which are strided in memory; the LDS transpose read
 // (ds_read_b64_tr_b16) turns the row-major slice into the K-contiguous
-// operand the MFMA needs.
+// operand the MFMA needs.  The query rows of the head (256 bytes each, one
+// row per n_heads * 256 bytes in memory) reach LDS in double-buffered blocks
+// of 64 by direct-to-LDS copies that read four whole rows each; their 16-byte
+// chunks are XOR-swizzled by row so the operand reads are free of bank
+// conflicts.
 //
-// The last workgroup of the grid builds the split plan for the attention
+// The first workgroup of the grid builds the split plan for the attention
 // kernel (the two are independent, so the plan costs no extra launch).
 #include "device_util.h"
 
@@ -29,20 +33,34 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ seq_lens, int max_blocks,
                                                           int batch, int sq, int n_heads, uint8_t* __restrict__ ws,
                                                           WsLayout Lw, int32_t* status) {
-  if (blockIdx.x == gridDim.x - 1) {
+  // block 0 builds the split plan: dispatched first, it overlaps the rest of the grid
+  if (blockIdx.x == 0) {
     plan_build(seq_lens, batch, sq, max_blocks, kBlk, Lw.align, Lw.W, ws, Lw, status);
     return;
   }
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNope * 256];   // W^UK_i slice: 128 rows x 128 cols bf16
+  // W^UK_i slice (128 rows x 128 cols bf16), then two 64-row blocks of query rows
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNope * 256 + 2 * 64 * kNope * 2];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
+  MLA_LDS uint8_t* qbuf = lds + kNope * 256;
   uint16_t* q_lat = (uint16_t*)(ws + Lw.off_qlat);
 
-  const int h = blockIdx.x >> 2;
-  const int cb = blockIdx.x & 3;      // 128-column block of the latent
+  // (head, 128-column block of the latent): the four blocks of a head take ids 8 apart, so
+  // they run on one XCD and share its L2 for the head's query rows
+  const int bid = blockIdx.x - 1;
+  const int full = (n_heads / 8) * 32;
+  int h, cb;
+  if (bid < full) {
+    h = 8 * (bid / 32) + bid % 8;
+    cb = (bid / 8) % 4;
+  } else {
+    h = (n_heads / 8) * 8 + (bid - full) / 4;
+    cb = (bid - full) % 4;
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int M = batch * sq;
+  const int nmb = (M + 63) / 64;      // 64-row blocks of query rows
 
   // stage the slice: LDS row d holds columns cb*128 .. +127 of W^UK row 128 h + d,
   // its 16-byte chunk k at chunk k ^ swz(d)
@@ -58,6 +76,24 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
       asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
     }
   }
+  // copy query-row block mb into buffer (mb & 1): LDS chunk P = 64 (wave + 4 k) + lane holds
+  // row P / 16 of the block, physical chunk P % 16 = logical chunk ^ (row % 16); rows past
+  // M re-read row M - 1
+  auto stage_q = [&](int mb) {
+    MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int P = 64 * (wave + 4 * k) + lane;
+      const int r = P >> 4;
+      int m = mb * 64 + r;
+      m = m < M ? m : M - 1;
+      const int c = (P & 15) ^ (r & 15);
+      const uint16_t* src = q_nope + ((size_t)m * n_heads + h) * kNope + 8 * c;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qb + (wave + 4 * k) * 1024));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
+    }
+  };
+  stage_q(0);
   // the rotary half of the latent query is a copy
   if (cb == 0) {
     for (int i = tid; i < M * (kRope / 8); i += 256) {
@@ -73,6 +109,7 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
   // columns 32 wave + 16 (g % 2) + 4 q .. +3, which the transpose hands out as
   // 4 consecutive d of column 32 wave + (lane % 32).
   const int hh = lane >> 5;
+  const int n = lane & 31;
   const int g16 = lane >> 4;
   const int e_ = (lane >> 2) & 3;
   const int q_ = lane & 3;
@@ -92,26 +129,31 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
     bop[ks] = u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
   }
 
-  const int n = lane & 31;
-  for (int mb = 0; mb * 32 < M; ++mb) {
-    const int m = mb * 32 + n;
-    f32x16 acc;
+  const int col = cb * 128 + 32 * wave + n;
+  for (int mb = 0; mb < nmb; ++mb) {
+    if (mb + 1 < nmb) stage_q(mb + 1);   // the next block lands while this one is multiplied
+    const MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    const uint16_t* qp = q_nope + ((size_t)m * n_heads + h) * kNope + 8 * hh;
+    for (int half = 0; half < 2; ++half) {
+      // A operand: lane reads query row 32 half + n of the block, d = 16 ks + 8 hh .. +7
+      const int r = 32 * half + n;
+      f32x16 acc;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 a = {0u, 0u, 0u, 0u};
-      if (m < M) a = *(const u32x4*)(qp + 16 * ks);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(bop[ks]), acc, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 a = *(const MLA_LDS u32x4*)(qb + r * (kNope * 2) + (((2 * ks + hh) ^ (r & 15)) * 16));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(bop[ks]), acc, 0, 0, 0);
+      }
+      // D[m][col]: lane holds column 32 wave + n, rows 8 (i/4) + 4 hh + i % 4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int mm = mb * 64 + 32 * half + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (mm < M) q_lat[((size_t)mm * n_heads + h) * kRow + col] = f2bf(acc[i]);
+      }
     }
-    // D[m][col]: lane holds column 32 wave + n, rows 8 (r/4) + 4 hh + r % 4
-    const int col = cb * 128 + 32 * wave + n;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      int mm = mb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (mm < M) q_lat[((size_t)mm * n_heads + h) * kRow + col] = f2bf(acc[r]);
-    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // next block landed (and this block's stores issued)
+    __syncthreads();                              // ... for every wave; this block's buffer is free
   }
 }
 
