@@ -18,8 +18,15 @@
 // keeps its Q (144 VGPRs) and its O accumulator (256 AGPRs) in registers for
 // the whole range, and every 16-byte LDS operand read feeds a full 32-row
 // MFMA.  The cache tile is read from HBM once per workgroup.
+//  - Software pipeline: iteration it scores stage it, then runs the latent
+//    product of stage it - 1 while the vector units compute stage it's
+//    softmax weights.  The score accumulators live in VGPRs (the score MFMAs
+//    are issued as asm in their VGPR form), the latent accumulators in AGPRs,
+//    so no accumulator is ever moved between the two register files.
 //  - Tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging)
-//    into a 4-deep ring of 36 KB stages, three stages in flight.
+//    into a 4-slot ring of 36 KB stages: one being multiplied, one being
+//    scored, two in flight.  A wave's copies are issued between its score
+//    MFMAs.
 //  - LDS rows are 1152 B.  16-byte chunk k of token row t sits at chunk
 //    k ^ sw(t), sw(t) = 2 (t mod 4) ^ ((t / 4) mod 8) (XOR within groups of 8
 //    chunks).  Measured with the LDS bank-conflict counter on gfx950, this
@@ -62,6 +69,23 @@ __device__ __forceinline__ const MLA_CONST T* as_const(const T* p) {
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
 
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Score MFMAs with their accumulators in VGPRs (the latent accumulators fill the
+// AGPRs).  Written as asm so that the choice is per instruction; the hazards
+// the compiler would otherwise handle are handled here: a chain starts from a
+// literal zero (no vector write precedes it), a chain accumulates in place with
+// the same opcode (back-to-back dependent issue is supported), and the results
+// are read only after settle_s's wait states.
+__device__ __forceinline__ void mfma_s_first(f32x16& acc, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& acc, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states: more than an 8- or 16-pass MFMA's result needs before a vector read
+__device__ __forceinline__ void settle_s(f32x16& a0, f32x16& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+}
 
 __device__ __forceinline__ u32x4 lds_read16(const MLA_LDS uint8_t* p) { return *(const MLA_LDS u32x4*)p; }
 
@@ -258,7 +282,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       return t < kSubTok - 1 ? t : kSubTok - 1;
     };
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < 2; ++k) {
       if (k < nsub) {
         issue_stage(k, stage_base(lookup_block(b, a + k * kSubTok), a + k * kSubTok), tlast_of(k));
       } else {
@@ -268,38 +292,45 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     }
     // block ids are looked up one stage ahead of their copies, so that the
     // scalar load's latency is hidden behind a whole stage of work
-    int blk_next = 3 < nsub ? lookup_block(b, a + 3 * kSubTok) : 0;
+    int blk_next = 2 < nsub ? lookup_block(b, a + 2 * kSubTok) : 0;
+    // softmax weights of the previous stage (bf16 pairs), consumed one iteration later
+    uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 
-    for (int it = 0; it < nsub; ++it) {
-      // This wave's copies of stage it have landed once at most two stages' worth
-      // (issued by the two previous iterations) remain in flight.
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoadsPerWave));
-      __syncthreads();   // all waves' copies of stage it visible; stage it - 1 fully consumed
-      // The copies of stage it + 3 ride along the score MFMAs below.  A ragged
+    // Iteration it scores stage it and, interleaved with that stage's softmax,
+    // runs the latent product of stage it - 1, so the softmax's vector work
+    // overlaps matrix work.  Iteration nsub only finishes the last product.
+    for (int it = 0; it <= nsub; ++it) {
+      // This wave's copies of stage it have landed once at most one stage's worth
+      // (issued by the previous iteration) remains in flight.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave));
+      __syncthreads();   // stage it visible to all waves; stage it - 2 fully consumed
+      // The copies of stage it + 2 ride along the score MFMAs below.  A ragged
       // stage (a sequence's last) goes out here in full, with its rows clamped.
       uint64_t nbase = idle_base;
       uint32_t ndst = idle_dst, nstride = 0;
-      if (it + 3 < nsub) {
-        const int tok = a + (it + 3) * kSubTok;
-        const int tl = tlast_of(it + 3);
+      if (it + 2 < nsub) {
+        const int tok = a + (it + 2) * kSubTok;
+        const int tl = tlast_of(it + 2);
         const uint64_t base = stage_base(blk_next, tok);
         if (tl == kSubTok - 1) {
           nbase = base;
-          ndst = (uint32_t)(uintptr_t)(lds + ((it + 3) & 3) * kStageBytes + wave * 1024);
+          ndst = (uint32_t)(uintptr_t)(lds + ((it + 2) & 3) * kStageBytes + wave * 1024);
           nstride = kWaves * 1024;
         } else {
-          issue_stage((it + 3) & 3, base, tl);
+          issue_stage((it + 2) & 3, base, tl);
         }
       }
-      if (it + 4 < nsub) blk_next = lookup_block(b, a + (it + 4) * kSubTok);
+      if (it + 3 < nsub) blk_next = lookup_block(b, a + (it + 3) * kSubTok);
+      const bool valid = it < nsub;
       const MLA_LDS uint8_t* st = lds + (it & 3) * kStageBytes;
+      // the latent product's stage (stage 0 for the empty product of iteration 0:
+      // finite data times zero weights)
+      const MLA_LDS uint8_t* sto = lds + ((it > 0 ? it - 1 : 0) & 3) * kStageBytes;
       const int tok0 = a + it * kSubTok;
 
       // ---- S^T = T . Q^T (32 tokens x 32 rows), 36 k-steps of 16 features
       // two independent accumulation chains (even / odd k-steps) keep the matrix core busy
       f32x16 acc_s, acc_s1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_s[r] = acc_s1[r] = 0.0f;
       {
         u32x4 tv[kPfS];
 #pragma unroll
@@ -308,33 +339,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
         for (int ks = 0; ks < 36; ++ks) {
           const u32x4 t = tv[ks % kPfS];
           if (ks + kPfS < 36) tv[ks % kPfS] = lds_read16(st + s_off[(ks + kPfS) & 3] + ((ks + kPfS) >> 2) * 128);
-          if (ks & 1) acc_s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(t), as_bf8(qreg[ks]), acc_s1, 0, 0, 0);
-          else acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(t), as_bf8(qreg[ks]), acc_s, 0, 0, 0);
+          if (ks < 2) mfma_s_first(ks & 1 ? acc_s1 : acc_s, t, qreg[ks]);
+          else mfma_s(ks & 1 ? acc_s1 : acc_s, t, qreg[ks]);
           if ((ks & 3) == 2)
             copy16_to_lds(nbase, ld_off(ks >> 2), __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
         }
-        // keep the operand reads kPfS ahead of the MFMAs that consume them
-#pragma unroll
-        for (int k = 0; k < kPfS; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (ks + kPfS < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        settle_s(acc_s, acc_s1);
       }
 
-      // ---- softmax weights against the row reference (log2 units).  Lane holds
+      // ---- softmax weights of stage it against the row reference (log2 units),
+      // interleaved below with the latent product of stage it - 1.  Lane holds
       // row n and tokens 8 (r / 4) + 4 hh + r % 4, r = 0..15.
       uint32_t pk[8];
       {
         float z[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) z[r] = (acc_s[r] + acc_s1[r]) * scale_log2;
-        if (tok0 + kSubTok - 1 > L - sq) {   // the stage reaches past some row's last visible token
+        if (!valid || tok0 + kSubTok - 1 > L - sq) {   // past some row's last visible token, or no stage
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int tok = tok0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            z[r] = tok > lim ? kNegInf : z[r];
+            z[r] = (!valid || tok > lim) ? kNegInf : z[r];
           }
         }
         float mx = z[0];
@@ -354,18 +379,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
         }
       }
 
-      // ---- O^T += C^T . P^T (512 features x 32 rows): 16 feature blocks x 2 token halves
+      // ---- O^T += C^T . P^T for stage it - 1 (512 features x 32 rows): 16 feature
+      // blocks x 2 token halves
       {
-        const u32x4 pb0 = {pk[0], pk[1], pk[2], pk[3]};
-        const u32x4 pb1 = {pk[4], pk[5], pk[6], pk[7]};
+        const u32x4 pb0 = {pk_prev[0], pk_prev[1], pk_prev[2], pk_prev[3]};
+        const u32x4 pb1 = {pk_prev[4], pk_prev[5], pk_prev[6], pk_prev[7]};
         // operand j: feature block fb = j & 15, token half hs = j >> 4; its two reads take
         // tokens 16 hs + 4 hh + e (r = 0) and 16 hs + 8 + 4 hh + e (r = 1)
         auto rd = [&](int j) {
           const int fb = j & 15, hs = j >> 4;
           const int o0 = (o_off[fb & 1] ^ (16 * (4 * hs))) + (fb >> 1) * 128 + (16 * hs) * (kRow * 2);
           const int o1 = (o_off[fb & 1] ^ (16 * (4 * hs + 2))) + (fb >> 1) * 128 + (16 * hs + 8) * (kRow * 2);
-          const u32x2 lo2 = lds_read_tr(st + o0);
-          const u32x2 hi2 = lds_read_tr(st + o1);
+          const u32x2 lo2 = lds_read_tr(sto + o0);
+          const u32x2 hi2 = lds_read_tr(sto + o1);
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         };
         u32x4 av[kPfO];
@@ -378,6 +404,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
           acc_o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(op), as_bf8(j < 16 ? pb0 : pb1),
                                                                   acc_o[j & 15], 0, 0, 0);
         }
+        // reads kPfO operands ahead; between consecutive MFMAs, a share of the softmax's vector work
 #pragma unroll
         for (int k = 0; k < kPfO; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -386,6 +413,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
           if (j + kPfO < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pk_prev[k] = pk[k];
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0ull && lane == 0) s_retry = 1;
     __syncthreads();   // ring free for the next range; every wave's flag visible
