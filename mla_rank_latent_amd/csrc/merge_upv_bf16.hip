@@ -37,11 +37,15 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
                                                              const uint8_t* __restrict__ ws, WsLayout Lw,
                                                              uint16_t* __restrict__ out, float* __restrict__ lse) {
   // hi and lo parts of the merged latent (32 rows x 512, swizzled 16-byte
-  // chunks), then the upper latent half's partial products (32 x 128 fp32)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kMergeRows * kLat * 2 + kMergeRows * kNope * 4];
+  // chunks), the upper latent half's partial products (32 x 128 fp32), and the
+  // slots' partial sums when rows are shared by several slots (32 x 512 fp32)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kMergeRows * kLat * 2 + kMergeRows * kNope * 4 +
+                                                         kMergeRows * kLat * 4];
+  __shared__ float s_mx[kMergeRows], s_den[kMergeRows];
   MLA_LDS uint8_t* s_hi = (MLA_LDS uint8_t*)smem;
   MLA_LDS uint8_t* s_lo = s_hi + kMergeRows * kLat * 2;
   MLA_LDS float* s_red = (MLA_LDS float*)(s_lo + kMergeRows * kLat * 2);
+  MLA_LDS uint8_t* s_comb = (MLA_LDS uint8_t*)(s_red + kMergeRows * kNope);
 
   const int M = batch * sq;
   const int h = blockIdx.x % n_heads;
@@ -63,70 +67,111 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     for (int ks = 0; ks < 16; ++ks) bop[ks] = *(const u32x4*)(wp + 16 * ks);
   }
 
-  // ---- merge: thread = (row i, column lane c16); columns 64 j + 4 c16 .. +3, j = 0..7
+  // ---- merge.  Sixteen threads (a slot) own one row's 512 columns: thread c16 of a slot
+  // holds columns 64 j + 4 c16 .. +3, j = 0..7.  With rv < 32 valid rows (small batches,
+  // whose sequences are split into many pieces) a row gets pl_n = 32 / rp slots (rp = rv
+  // rounded up to a power of two) that take every pl_n-th piece; their maxima and then
+  // their weighted sums are combined through LDS in slot order.
   {
-    const int i = tid >> 4;
+    const int rv = M - mb * kMergeRows < kMergeRows ? M - mb * kMergeRows : kMergeRows;
+    int rp = 1;
+    while (rp < rv) rp <<= 1;
+    const int pl_n = kMergeRows / rp;
+    const int slot = tid >> 4;
     const int c16 = tid & 15;
+    const int i = slot % rp;          // row within the block
+    const int pl = slot / rp;         // piece lane of the row
     const int m = mb * kMergeRows + i;
+    const bool row_ok = i < rv;
+    if (rv < kMergeRows) {
+      // rows without a slot (or past M) must still hold finite values for the MFMAs
+      for (int k = tid; k < kMergeRows * kLat / 4; k += 512) {
+        ((MLA_LDS u32x2*)s_hi)[k] = u32x2{0u, 0u};
+        ((MLA_LDS u32x2*)s_lo)[k] = u32x2{0u, 0u};
+      }
+      __syncthreads();   // the rows' own values land after the fill
+    }
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float den = 0.0f, Mx = -__builtin_inff();
-    if (m < M) {
+    int p0 = 0, p1 = 0, r = 0;
+    const float2* part_ml = (const float2*)(ws + Lw.off_lse);
+    const float* part_o = (const float*)(ws + Lw.off_o);
+    if (row_ok) {
       const int b = m / sq;
       const int s = m - b * sq;
       const int g = h / hg;
-      const int r = (h - g * hg) * sq + s;
+      r = (h - g * hg) * sq + s;
       const int32_t* piece_base = (const int32_t*)(ws + Lw.off_piece);
-      const float2* part_ml = (const float2*)(ws + Lw.off_lse);
-      const float* part_o = (const float*)(ws + Lw.off_o);
-      const int p0 = g * P + piece_base[b];
-      const int p1 = g * P + piece_base[b + 1];
-      for (int p = p0; p < p1; ++p) {
+      p0 = g * P + piece_base[b];
+      p1 = g * P + piece_base[b + 1];
+      for (int p = p0 + pl; p < p1; p += pl_n) {
         const float2 ml = part_ml[(size_t)p * Lw.rows + r];
         if (ml.y > 0.0f) Mx = fmaxf(Mx, ml.x);
       }
-      if (Mx != -__builtin_inff()) {
-        for (int p = p0; p < p1; p += 2) {
-          // the second piece of the pair; past the end it re-reads piece p with weight 0
-          const int q = p + 1 < p1 ? p + 1 : p;
-          const float2 ml0 = part_ml[(size_t)p * Lw.rows + r];
-          const float2 ml1 = part_ml[(size_t)q * Lw.rows + r];
-          const f32x4* o0 = (const f32x4*)(part_o + ((size_t)p * Lw.rows + r) * kLat) + c16;
-          const f32x4* o1 = (const f32x4*)(part_o + ((size_t)q * Lw.rows + r) * kLat) + c16;
-          f32x4 v0[8], v1[8];
+    }
+    if (pl_n > 1) {   // the row's maximum over all of its slots
+      if (c16 == 0) s_mx[slot] = Mx;
+      __syncthreads();
+      for (int q = 0; q < pl_n; ++q) Mx = fmaxf(Mx, s_mx[q * rp + i]);
+    }
+    if (row_ok && Mx != -__builtin_inff()) {
+      for (int p = p0 + pl; p < p1; p += 2 * pl_n) {
+        // the second piece of the pair; past the end it re-reads piece p with weight 0
+        const int q = p + pl_n < p1 ? p + pl_n : p;
+        const float2 ml0 = part_ml[(size_t)p * Lw.rows + r];
+        const float2 ml1 = part_ml[(size_t)q * Lw.rows + r];
+        const f32x4* o0 = (const f32x4*)(part_o + ((size_t)p * Lw.rows + r) * kLat) + c16;
+        const f32x4* o1 = (const f32x4*)(part_o + ((size_t)q * Lw.rows + r) * kLat) + c16;
+        f32x4 v0[8], v1[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v0[j] = o0[16 * j];
+        for (int j = 0; j < 8; ++j) v0[j] = o0[16 * j];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v1[j] = o1[16 * j];
-          // an empty piece has l = 0, m = -inf and O = 0: weight 0
-          const float w0 = ml0.y > 0.0f ? __builtin_amdgcn_exp2f(ml0.x - Mx) : 0.0f;
-          const float w1 = (q != p && ml1.y > 0.0f) ? __builtin_amdgcn_exp2f(ml1.x - Mx) : 0.0f;
-          den += w0 * ml0.y + w1 * ml1.y;
+        for (int j = 0; j < 8; ++j) v1[j] = o1[16 * j];
+        // an empty piece has l = 0, m = -inf and O = 0: weight 0
+        const float w0 = ml0.y > 0.0f ? __builtin_amdgcn_exp2f(ml0.x - Mx) : 0.0f;
+        const float w1 = (q != p && ml1.y > 0.0f) ? __builtin_amdgcn_exp2f(ml1.x - Mx) : 0.0f;
+        den += w0 * ml0.y + w1 * ml1.y;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += w0 * v0[j] + w1 * v1[j];
+        for (int j = 0; j < 8; ++j) acc[j] += w0 * v0[j] + w1 * v1[j];
+      }
+    }
+    if (pl_n > 1) {   // sum the row's slots in slot order
+      MLA_LDS f32x4* comb = (MLA_LDS f32x4*)s_comb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) comb[(slot * 16 + c16) * 8 + j] = acc[j];
+      if (c16 == 0) s_den[slot] = den;
+      __syncthreads();
+      if (pl == 0) {
+        for (int q = 1; q < pl_n; ++q) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] += comb[((q * rp + i) * 16 + c16) * 8 + j];
+          den += s_den[q * rp + i];
         }
       }
+    }
+    if (row_ok && pl == 0) {
       if (c16 == 0 && lse != nullptr)
         lse[(size_t)m * n_heads + h] =
             den > 0.0f ? (Mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    // columns 64 j + 4 c16 .. +3 are half (c16 & 1) of logical chunk 8 j + c16 / 2,
-    // stored at chunk 8 j + ((c16 / 2) ^ (i % 8))
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      // columns 64 j + 4 c16 .. +3 are half (c16 & 1) of logical chunk 8 j + c16 / 2,
+      // stored at chunk 8 j + ((c16 / 2) ^ (i % 8))
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x2 vh, vl;
+      for (int j = 0; j < 8; ++j) {
+        u32x2 vh, vl;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float x0 = acc[j][2 * e] * inv, x1 = acc[j][2 * e + 1] * inv;
-        const uint32_t hp = pack_bf2(x0, x1);
-        vh[e] = hp;
-        vl[e] = pack_bf2(x0 - bf2f((uint16_t)(hp & 0xffffu)), x1 - bf2f((uint16_t)(hp >> 16)));
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = acc[j][2 * e] * inv, x1 = acc[j][2 * e + 1] * inv;
+          const uint32_t hp = pack_bf2(x0, x1);
+          vh[e] = hp;
+          vl[e] = pack_bf2(x0 - bf2f((uint16_t)(hp & 0xffffu)), x1 - bf2f((uint16_t)(hp >> 16)));
+        }
+        const int off = i * (kLat * 2) + (8 * j + ((c16 >> 1) ^ (i & 7))) * 16 + 8 * (c16 & 1);
+        *(MLA_LDS u32x2*)(s_hi + off) = vh;
+        *(MLA_LDS u32x2*)(s_lo + off) = vl;
       }
-      const int off = i * (kLat * 2) + (8 * j + ((c16 >> 1) ^ (i & 7))) * 16 + 8 * (c16 & 1);
-      *(MLA_LDS u32x2*)(s_hi + off) = vh;
-      *(MLA_LDS u32x2*)(s_lo + off) = vl;
     }
   }
   __syncthreads();
