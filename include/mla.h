@@ -28,7 +28,8 @@
  *    its table row) are never turned into out-of-bounds accesses: the access
  *    is clamped or skipped and the matching MLA_STATUS_* bit is OR-ed into
  *    the optional device word `status`.
- *  - The library holds no mutable global state; concurrent calls on different
+ *  - The library's only mutable global state is a per-device cache of the
+ *    compute-unit count (written once, atomically); concurrent calls on different
  *    streams are safe as long as they do not share output or workspace memory.
  */
 #ifndef MLA_H_
@@ -75,9 +76,9 @@ typedef struct mla_dims {
 /*
  * Size limits.
  *  - MLA_DTYPE_BF16 runs the MFMA kernels, built for DeepSeek-V2's widths:
- *    d_nope = 128, d_rope = 64, d_latent = 512, block_size = 64, n_heads a
- *    multiple of 16 up to 128, d_model a multiple of 64, sq in 1..8.  Other
- *    bf16 dims give MLA_ERR_UNSUPPORTED.
+ *    d_nope = 128, d_rope = 64, d_latent = 512, block_size = 64, n_heads in
+ *    1..1024, d_model a multiple of 32, sq in 1..8.  Other bf16 dims give
+ *    MLA_ERR_UNSUPPORTED (sq above 8: MLA_ERR_CAPACITY).
  *  - MLA_DTYPE_F32 runs plain fp32 kernels for any dims with d_nope, d_rope
  *    (even) and d_latent in 1..1024, d_latent + d_rope <= 1024,
  *    n_heads <= 1024, block_size 1..1024, sq in 1..64.
