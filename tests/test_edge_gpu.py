@@ -108,3 +108,25 @@ def test_bad_append_position_is_reported_and_skipped(split):
     blk0 = x["block_table"][0, p0 // 64]
     changed = np.argwhere(np.any(after != before, axis=-1))
     assert [tuple(r) for r in changed] == [(blk0, p0 % 64)]     # only sequence 0's row was written
+
+
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_late_dominant_token_restarts_the_range(num_splits):
+    """One token, late in its range, whose rotary key is scaled 60x: for most heads
+    its score beats the range's first-stage maximum by far more than 2^16, which
+    makes the kernel re-run the range against the larger reference.  The latent
+    values are untouched, so the output keeps its usual magnitude."""
+    spec = H.small_spec("late_spike", 2, 1, [500, 300], seed=51)
+
+    def mutate(x):
+        pool = synth.bf16_bits_to_f32(x["pool"]).copy()
+        t = 400                                    # past the first stage of its range in both split counts
+        blk = x["block_table"][0, t // 64]
+        pool[blk, t % 64, 512:] *= 60.0
+        x["pool"] = synth.f32_to_bf16_bits(pool.astype(np.float32))
+
+    x, c = _run(spec, num_splits=num_splits, mutate=mutate)
+    assert int(c.status.item()) == 0
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", f"late_spike splits={num_splits}")
+    assert np.max(np.abs(H.host(c.lse) - lse) / np.maximum(np.abs(lse), 1.0)) <= 2e-2
