@@ -98,8 +98,10 @@ __device__ __forceinline__ u32x2 lds_read_tr(const MLA_LDS uint8_t* p) {
 // address = m0 + 16 * lane.  Issued as asm so that the compiler does not
 // treat every later LDS read as aliasing the copy (it would then wait for all
 // copies in flight); the ring protocol waits for exactly the stage it reads.
+// The cache stream is read once, so it is marked non-temporal: it then
+// displaces less of what the step's other kernels re-read from the caches.
 __device__ __forceinline__ void copy16_to_lds(uint64_t base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds_addr)
                : "memory");
 }
 
