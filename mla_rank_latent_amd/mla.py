@@ -27,6 +27,17 @@ EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_a
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or python -m mla_rank_latent_amd.build)")
+# The library must run on the same HIP runtime as the tensors and streams it is
+# handed.  torch's HIP library is requested by file name (libamdhip64.so) but
+# carries the soname libamdhip64.so.7, which is what the library asks for: with
+# torch loaded first the loader binds the library to torch's runtime; loaded the
+# other way round, the process would hold two HIP (and HSA) runtimes, and the
+# library's device queries and launches would go to one that does not own the
+# tensors.  So torch, when installed, is imported before the library is opened.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    torch = None
 _lib = ctypes.CDLL(LIB_PATH)
 
 

@@ -20,6 +20,21 @@ def test_exports_every_declared_function():
         assert hasattr(lib, name), name
 
 
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the binding before torch must not leave a second HIP runtime in
+    the process (the library would then query and launch on a runtime that does
+    not own torch's tensors and streams)."""
+    import subprocess
+    import sys
+    code = ("from mla_rank_latent_amd import mla\n"
+            "import torch\n"
+            "maps = set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)\n"
+            "print(len(maps))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
 def test_status_strings():
     codes = [0, -1, -2, -3, -4, -5, -6, -7, -8]
     strs = [mla.mla_status_str(c) for c in codes]
