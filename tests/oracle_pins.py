@@ -322,3 +322,73 @@ def pin_query_key_rotation_alignment(orc) -> float:
 
 
 ALL_PINS.append(pin_query_key_rotation_alignment)
+
+
+def _causal_mha_loops(x, wq, wk, wv, H, D):
+    """Causal self-attention over every position t of x [L, d]: position t
+    attends positions 0..t, softmax(q k^T / sqrt(D)) v per head, as loops."""
+    L, d = x.shape
+
+    def proj(w, t, row):
+        return sum(w[row][c] * x[t][c] for c in range(d))
+    out = np.zeros((L, H, D))
+    for t in range(L):
+        for hh in range(H):
+            q = [proj(wq, t, hh * D + e) for e in range(D)]
+            z = []
+            for u in range(t + 1):
+                k = [proj(wk, u, hh * D + e) for e in range(D)]
+                z.append(sum(q[e] * k[e] for e in range(D)) / math.sqrt(D))
+            mx = max(z)
+            w = [math.exp(zz - mx) for zz in z]
+            s = sum(w)
+            for u in range(t + 1):
+                v = [proj(wv, u, hh * D + e) for e in range(D)]
+                for e in range(D):
+                    out[t, hh, e] += w[u] / s * v[e]
+    return out
+
+
+def pin_prefill_causal_mha(orc) -> float:
+    """Prefill: every token of a sequence is a query (a query group of the whole
+    length).  With the MHA special case of the append and decompression weights
+    (W^DKV = [W_K; W_V], W^UK = [I 0], W^UV = [0 I], no rotary part), position t
+    must equal textbook causal self-attention over positions 0..t, checked
+    against explicit loops for every position, in two sequences of different
+    lengths sharing one permuted pool."""
+    rng = _rng(13)
+    H, D, d, dr, bs = 2, 3, 5, 2, 4
+    lens = [7, 10]
+    dc = 2 * H * D
+    wq, wk, wv = (rng.standard_normal((H * D, d)) for _ in range(3))
+    w_dkv = np.concatenate([wk, wv], axis=0)
+    eye = np.eye(H * D)
+    w_uk = np.concatenate([eye, np.zeros((H * D, H * D))], axis=1)
+    w_uv = np.concatenate([np.zeros((H * D, H * D)), eye], axis=1)
+    w_kr = np.zeros((dr, d))
+    w_qr = np.zeros((H * dr, d))
+    nblk = [(L + bs - 1) // bs for L in lens]
+    perm = rng.permutation(sum(nblk))
+    bt = np.full((2, max(nblk)), -1, dtype=np.int64)
+    bt[0, :nblk[0]] = perm[:nblk[0]]
+    bt[1, :nblk[1]] = perm[nblk[0]:]
+    pool = np.full((sum(nblk), bs, dc + dr), 7.0)
+    Lm = max(lens)
+    xs = [rng.standard_normal((L, d)) for L in lens]
+    qn = np.zeros((2, Lm, H, D))
+    qr = np.zeros((2, Lm, H, dr))
+    err = 0.0
+    for b, (L, x) in enumerate(zip(lens, xs)):
+        pos = np.arange(L)[None, :]
+        rows = orc.cache_rows(x[None], w_dkv, w_kr, pos, 10000.0, "f64")
+        orc.write_rows(pool, bt[b:b + 1], pos, rows, bs)
+    for b, (L, x) in enumerate(zip(lens, xs)):
+        pos = np.arange(L)[None, :]
+        qn_b, qr_b = orc.q_project(x[None], wq, w_qr, pos, H, 10000.0)
+        out, lse = orc.decode(qn_b, qr_b, w_uk, w_uv, pool, bt[b:b + 1], [L], 1.0 / math.sqrt(D), bs)
+        ref = _causal_mha_loops(x, wq, wk, wv, H, D)
+        err = max(err, float(np.max(np.abs(out[0] - ref))))
+    return err
+
+
+ALL_PINS.append(pin_prefill_causal_mha)

@@ -55,6 +55,8 @@ MUTANTS = {
     "rope_key_dropped": ("k = np.concatenate([c @ wk.T, kr], axis=1)", "k = np.concatenate([c @ wk.T, 0 * kr], axis=1)"),
     "causal_off_by_one": ("                n = L - Sq + s + 1\n                if n <= 0:\n                    out[b, s, i], lse[b, s, i] = 0.0, -np.inf\n                    continue\n                q = np.concatenate",
                           "                n = L - Sq + s + (s == 0)\n                if n <= 0:\n                    out[b, s, i], lse[b, s, i] = 0.0, -np.inf\n                    continue\n                q = np.concatenate"),
+    "causal_group_sees_all": ("                n = L - Sq + s + 1\n                if n <= 0:",
+                              "                n = L\n                if n <= 0:"),
     "scale_dropped": ("_softmax_attend(scale * (k[:n] @ q), v[:n])", "_softmax_attend((k[:n] @ q), v[:n])"),
     "softmax_unnormalised": ("return (e / den) @ v, m + math.log(den)", "return (e / len(e)) @ v, m + math.log(den)"),
     "bf16_nine_bits": ("return _round_significand(x, 8, -126, 127)", "return _round_significand(x, 9, -126, 127)"),
