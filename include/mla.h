@@ -226,6 +226,45 @@ int mla_decode_finish(const mla_dims* dims, const void* q_nope, const void* q_ro
                       void* workspace, size_t workspace_bytes, void* out, float* lse,
                       int32_t* status, void* stream);
 
+/*
+ * Workspace bytes mla_prefill needs: the expanded per-head keys and values of
+ * every token slot the block table can address,
+ *   2 * batch * n_heads * (max_blocks * block_size) * d_nope * 2 bytes.
+ * bf16 only; returns 0 for invalid arguments or f32 dims.
+ */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_blocks);
+
+/*
+ * Prefill attention in expanded form for the last `t` tokens of each sequence
+ * ("DeepSeek-V2 ... MLA" page §2.1 up-projections, §3.2 decoupled RoPE).  The
+ * result is the attention mla_decode defines for a query group of t tokens;
+ * the computation decompresses instead of absorbing, which is the cheaper
+ * order when many queries read each cached token:
+ *   k^C_{j,i} = W^UK_i c_j,  v_{j,i} = W^UV_i c_j          (every context token j)
+ *   z_j    = scale * ([q^C_i ‖ q^R_i] . [k^C_{j,i} ‖ k^R_j])
+ *   out_i  = sum_j softmax(z)_j v_{j,i}
+ * Query s of sequence b sits at position seq_lens[b] - t + s and sees tokens
+ * 0 .. seq_lens[b] - t + s.  The t new tokens' rows must already be in the
+ * cache (mla_cache_append with the same t).
+ *
+ * q_nope     [batch, t, n_heads, d_nope]   bf16
+ * q_rope     [batch, t, n_heads, d_rope]   bf16, already rotated
+ * w_uk, w_uv, cache, block_table, seq_lens, softmax_scale, lse, status: as for
+ *            mla_decode
+ * t          query tokens per sequence, 1 .. max_blocks * block_size
+ * workspace  device scratch of at least mla_prefill_workspace_bytes(dims,
+ *            batch, max_blocks) bytes, 256-byte aligned; clobbered
+ * out        [batch, t, n_heads, d_nope]   bf16
+ * Limits: bf16 dims only (f32: MLA_ERR_UNSUPPORTED);
+ * max_blocks * block_size <= 2^23.
+ */
+int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                int32_t batch, int32_t t, float softmax_scale,
+                void* workspace, size_t workspace_bytes, void* out, float* lse,
+                int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

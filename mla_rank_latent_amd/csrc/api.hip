@@ -254,4 +254,51 @@ int mla_decode_prepare(MLA_DECODE_PARAMS) { return decode_phases(kPhasePrepare, 
 int mla_decode_attend(MLA_DECODE_PARAMS) { return decode_phases(kPhaseAttend, MLA_DECODE_ARGS); }
 int mla_decode_finish(MLA_DECODE_PARAMS) { return decode_phases(kPhaseFinish, MLA_DECODE_ARGS); }
 
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_blocks) {
+  if (check_dims(dims) != MLA_OK || dims->dtype != MLA_DTYPE_BF16 || batch < 1 || batch > 65536 || max_blocks < 1 ||
+      (long long)max_blocks * dims->block_size > (1ll << 23))
+    return 0;
+  return prefill_ws_bytes(batch, dims->n_heads, max_blocks);
+}
+
+int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
+                const void* cache, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                const int32_t* seq_lens, int32_t batch, int32_t t, float softmax_scale, void* workspace,
+                size_t workspace_bytes, void* out, float* lse, int32_t* status, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if (dims->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!q_nope || !q_rope || !w_uk || !w_uv || !cache || !block_table || !seq_lens || !workspace || !out)
+    return MLA_ERR_NULL_PTR;
+  if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
+  if ((long long)max_blocks * dims->block_size > (1ll << 23)) return MLA_ERR_CAPACITY;
+  if (t < 1 || (long long)t > (long long)max_blocks * dims->block_size || !std::isfinite(softmax_scale))
+    return MLA_ERR_BAD_DIMS;
+  if ((long long)batch * t * dims->n_heads >= (1ll << 31)) return MLA_ERR_CAPACITY;
+  {
+    // launch grids: (sequence, 128-token tile, head) and (sequence x head rounded to 8, 256-row query tile)
+    const long long tiles = ((long long)max_blocks * dims->block_size + 127) / 128;
+    const long long qtiles = ((long long)t + 255) / 256;
+    if ((long long)batch * tiles * dims->n_heads >= (1ll << 31) ||
+        ((long long)batch * dims->n_heads + 7) / 8 * 8 * qtiles >= (1ll << 31))
+      return MLA_ERR_CAPACITY;
+  }
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(cache) ||
+      !aligned16(block_table) || !aligned16(seq_lens) || !aligned16(out) || ((uintptr_t)workspace & (kAlign - 1)) ||
+      (lse && ((uintptr_t)lse & 3u)) || (status && ((uintptr_t)status & 3u)))
+    return MLA_ERR_BAD_ALIGN;
+  const size_t need = prefill_ws_bytes(batch, dims->n_heads, max_blocks);
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t* kc = (uint16_t*)workspace;
+  uint16_t* vt = kc + need / 4;   // the second half: V^T
+  hipError_t e = launch_expand_kv_bf16((const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch,
+                                       dims->n_heads, (const uint16_t*)w_uk, (const uint16_t*)w_uv, kc, vt, status, st);
+  if (e == hipSuccess)
+    e = launch_prefill_attn_bf16((const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)cache,
+                                 num_blocks, block_table, max_blocks, seq_lens, batch, t, dims->n_heads,
+                                 softmax_scale, kc, vt, (uint16_t*)out, lse, status, st);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -85,6 +85,16 @@ hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_bl
                             hipStream_t st);
 hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads,
                                  uint8_t* ws, uint16_t* out, float* lse, hipStream_t st);
+// prefill (expanded form): workspace bytes, K^C / V^T expansion, causal attention
+size_t prefill_ws_bytes(int batch, int n_heads, int max_blocks);
+hipError_t launch_expand_kv_bf16(const uint16_t* cache, int num_blocks, const int32_t* block_table, int max_blocks,
+                                 const int32_t* seq_lens, int batch, int n_heads, const uint16_t* w_uk,
+                                 const uint16_t* w_uv, uint16_t* kc, uint16_t* vt, int32_t* status, hipStream_t st);
+hipError_t launch_prefill_attn_bf16(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* cache,
+                                    int num_blocks, const int32_t* block_table, int max_blocks,
+                                    const int32_t* seq_lens, int batch, int t, int n_heads, float scale,
+                                    const uint16_t* kc, const uint16_t* vt, uint16_t* out, float* lse,
+                                    int32_t* status, hipStream_t st);
 hipError_t launch_decode_f32(int phases, const mla_dims* d, const WsLayout& L, const float* q_nope, const float* q_rope,
                              const float* w_uk, const float* w_uv, const float* cache, int num_blocks,
                              const int32_t* block_table, int max_blocks, const int32_t* seq_lens,

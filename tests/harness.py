@@ -108,6 +108,36 @@ class GpuCase:
         self.decode()
 
 
+class PrefillCase:
+    """Device copies of a generated workload whose sq query tokens are a prefill chunk."""
+
+    def __init__(self, x: dict):
+        import torch
+        from mla_rank_latent_amd import mla
+        self.x = x
+        self.spec = spec = x["spec"]
+        self.d = mla_dims(spec)
+        self.pool = dev(x["pool"], spec.dtype)
+        self.block_table = dev(x["block_table"], spec.dtype)
+        self.seq_lens = dev(x["seq_lens"], spec.dtype)
+        self.w_uk = dev(x["w_uk"], spec.dtype)
+        self.w_uv = dev(x["w_uv"], spec.dtype)
+        self.q_nope = dev(x["q_nope"], spec.dtype)
+        self.q_rope = dev(x["q_rope"], spec.dtype)
+        B, T, H = spec.batch, spec.sq, spec.n_heads
+        self.out = torch.empty(B, T, H, spec.d_nope, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nbytes = mla.mla_prefill_workspace_bytes(self.d, B, int(x["block_table"].shape[1]))
+        assert nbytes > 0
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def run(self):
+        from mla_rank_latent_amd import mla
+        mla.mla_prefill(self.d, self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.pool, self.block_table,
+                        self.seq_lens, self.x["scale"], self.ws, self.out, lse=self.lse, status=self.status)
+
+
 # ---------------------------------------------------------------------------
 # oracle side
 # ---------------------------------------------------------------------------
@@ -142,6 +172,24 @@ def oracle_decode(x: dict, batches=None, heads=None, appended_rows=None, q=None)
                                  x["scale"], bs, heads=heads)
         out[b], lse[b] = o[0], l[0]
     return out, lse
+
+
+def oracle_query_samples(x: dict, samples):
+    """Oracle out [d_h] and lse for sampled (b, s, h): query s of sequence b's group is a single
+    query over the first L - Sq + s + 1 tokens (the causal rule of a query group)."""
+    spec = x["spec"]
+    bs = spec.block_size
+    qn, qr = synth.as_float(x["q_nope"], spec.dtype), synth.as_float(x["q_rope"], spec.dtype)
+    w_uk, w_uv = synth.as_float(x["w_uk"], spec.dtype), synth.as_float(x["w_uv"], spec.dtype)
+    res = []
+    for b, s, h in samples:
+        n = int(x["seq_lens"][b]) - spec.sq + s + 1
+        nblk = (n + bs - 1) // bs
+        sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)
+        o, l = mla_oracle.decode(qn[b:b + 1, s:s + 1], qr[b:b + 1, s:s + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :],
+                                 [n], x["scale"], bs, heads=[h])
+        res.append((o[0, 0, h], l[0, 0, h]))
+    return res
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:
