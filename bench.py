@@ -79,6 +79,160 @@ def workload_bytes_flops(spec, seq_lens):
     return dict(bytes=total_bytes, flops=total_flops, cache_bytes=cache, attn_flops=attn_flops, tokens=tokens)
 
 
+def prefill_flops(spec, seq_lens):
+    """Algorithmic flops of one prefill step: the append of the t new rows, the expansion of
+    every context token into per-head K^C and V, and causal attention (scores over 192
+    features and values of 128 per visible (query, key) pair and head)."""
+    H, dn, dr, dc, d = spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model
+    T = spec.sq
+    tokens = int(sum(int(L) for L in seq_lens))
+    pairs = 0
+    for L in seq_lens:
+        L = int(L)
+        pairs += sum(max(0, L - T + s + 1) for s in range(T))
+    append = 2 * spec.batch * T * (dc + dr) * d
+    expand = 2 * 2 * tokens * H * dn * dc
+    attn = 2 * H * pairs * (dn + dr + dn)
+    return dict(total=append + expand + attn, append=append, expand=expand, attn=attn, pairs=pairs)
+
+
+def cpu_baseline_prefill(x, budget_s: float):
+    """Time the fp64 oracle on the prefill workload: the appended rows, then whole heads
+    (every query of the sequence) until ``budget_s`` is spent; TFLOP/s of the same
+    algorithmic flops (the append counted once, expansion and attention per head)."""
+    import numpy as np
+    from mla_rank_latent_amd import synth
+    from oracle import mla_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = x["spec"]
+    bs = spec.block_size
+    L = int(x["seq_lens"][0])
+    nblk = (L + bs - 1) // bs
+    t0 = time.perf_counter()
+    rows = mla_oracle.cache_rows(synth.as_float(x["h"][:1], spec.dtype), synth.as_float(x["w_dkv"], spec.dtype),
+                                 synth.as_float(x["w_kr"], spec.dtype), x["positions"][:1], spec.rope_base, spec.dtype)
+    sub = synth.as_float(x["pool"][x["block_table"][0, :nblk]], spec.dtype)
+    for t, p in enumerate(x["positions"][0]):
+        sub[p // bs, p % bs] = rows[0, t]
+    spent = time.perf_counter() - t0
+    qn, qr = synth.as_float(x["q_nope"][:1], spec.dtype), synth.as_float(x["q_rope"][:1], spec.dtype)
+    w_uk, w_uv = synth.as_float(x["w_uk"], spec.dtype), synth.as_float(x["w_uv"], spec.dtype)
+    heads = 0
+    for hh in range(spec.n_heads):
+        t0 = time.perf_counter()
+        mla_oracle.decode(qn, qr, w_uk, w_uv, sub, np.arange(nblk)[None, :], [L], x["scale"], bs, heads=[hh])
+        spent += time.perf_counter() - t0
+        heads += 1
+        if spent >= budget_s:
+            break
+    f = prefill_flops(spec, x["seq_lens"][:1])
+    done = f["append"] / spec.batch + (f["expand"] + f["attn"]) / spec.batch * heads / spec.n_heads
+    return {"value": round(done / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequence 0: its {spec.sq} appended rows and {heads} of {spec.n_heads} heads (every query) "
+                      f"in {spent:.1f} s; fp64 numpy; TFLOP/s of the same algorithmic flops"}
+
+
+def run_prefill(args, spec, x) -> int:
+    """Prefill leg: one step = append of the t new rows of every sequence, expansion of the
+    context into per-head K^C and V, causal attention of the t queries."""
+    import torch
+    from mla_rank_latent_amd import mla
+
+    def dev(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, spec.dtype,
+                 spec.rope_base)
+    pool, bt, lens = dev(x["pool"]), dev(x["block_table"]), dev(x["seq_lens"])
+    w_uk, w_uv = dev(x["w_uk"]), dev(x["w_uv"])
+    qn, qr = dev(x["q_nope"]), dev(x["q_rope"])
+    h, w_dkv, w_kr, pos = dev(x["h"]), dev(x["w_dkv"]), dev(x["w_kr"]), dev(x["positions"])
+    out = torch.empty(spec.batch, spec.sq, spec.n_heads, spec.d_nope, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(spec.batch, spec.sq, spec.n_heads, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.mla_prefill_workspace_bytes(d, spec.batch, int(bt.shape[1])), dtype=torch.uint8,
+                     device="cuda")
+    n_ws = mla.mla_cache_append_workspace_bytes(d, int(h.shape[0]), int(h.shape[1]))
+    append_ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    append = mla.prepared_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, workspace=append_ws, stream=stream)
+    pargs = (d, qn, qr, w_uk, w_uv, pool, bt, lens, x["scale"], ws, out)
+    expand = mla.prepared_prefill("mla_prefill_expand", *pargs, lse=lse, stream=stream)
+    attend = mla.prepared_prefill("mla_prefill_attend", *pargs, lse=lse, stream=stream)
+
+    def step(ev_a=None, ev_b=None):
+        append()
+        expand()
+        if ev_a is not None:
+            ev_a.record(stream)
+        attend()
+        if ev_b is not None:
+            ev_b.record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(ev_a[i], ev_b[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_attn = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
+          f"attention {ms_attn * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    f = prefill_flops(spec, x["seq_lens"])
+    step_s = ms_step * 1e-3
+    tflops = f["total"] / step_s / 1e12
+    attn_tflops = f["attn"] / (ms_attn * 1e-3) / 1e12
+    res = {
+        "metric": "MLA prefill TFLOP/s (% of bf16 MFMA peak), tokens/s; B=1 ctx=8K 128 heads, every token a query",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) queries/hidden states, N(0,1/fan_in) weights)",
+        "config": {"workload": spec.name, "batch": spec.batch, "context": int(max(x["seq_lens"])),
+                   "query_tokens": spec.sq, "heads": spec.n_heads, "d_latent": spec.d_latent,
+                   "d_rope": spec.d_rope, "d_nope": spec.d_nope, "d_model": spec.d_model,
+                   "block_size": spec.block_size, "paged": spec.paged, "append": spec.append},
+        "tokens_per_s": round(spec.batch * spec.sq / step_s, 1),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "step_flops": f["total"],
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
+                     "flops_per_launch": f["attn"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (oracle, ~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_prefill(x, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def cpu_baseline(x, budget_s: float):
     """Time the fp64 oracle (as it stands) on whole sequences of the workload until
     ``budget_s`` of CPU work has been spent; scale to GB/s of the same algorithmic bytes."""
@@ -150,9 +304,12 @@ def main() -> int:
         print(json.dumps({"copy_bytes_per_dispatch": 1 << 30, "dispatches": 3}), flush=True)
         return 0
 
-    spec = synth.presets()[args.workload]
+    prefill = synth.prefill_presets()
+    spec = prefill[args.workload] if args.workload in prefill else synth.presets()[args.workload]
     print(f"[bench] generating {spec.name} (seed {spec.seed})", file=sys.stderr, flush=True)
     x = synth.make_inputs(spec)
+    if args.workload in prefill:
+        return run_prefill(args, spec, x)
 
     def dev(a):
         import numpy as np

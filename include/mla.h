@@ -265,6 +265,28 @@ int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope,
                 void* workspace, size_t workspace_bytes, void* out, float* lse,
                 int32_t* status, void* stream);
 
+/*
+ * The two phases of mla_prefill, for callers that schedule or time them
+ * separately.  Same arguments, checks and conventions; calling both in order
+ * on one stream with the same arguments and workspace is exactly mla_prefill.
+ *  - expand: k^C_{j,i} = W^UK_i c_j and v_{j,i} = W^UV_i c_j for every context
+ *    token j and head i ("DeepSeek-V2 ... MLA" page §2.1), into the workspace.
+ *  - attend: causal attention of the t queries over [k^C_{j,i} ‖ k^R_j] and
+ *    v_{j,i} (§3.2); writes out and lse.
+ */
+int mla_prefill_expand(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                       const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                       const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                       int32_t batch, int32_t t, float softmax_scale,
+                       void* workspace, size_t workspace_bytes, void* out, float* lse,
+                       int32_t* status, void* stream);
+int mla_prefill_attend(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                       const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                       const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                       int32_t batch, int32_t t, float softmax_scale,
+                       void* workspace, size_t workspace_bytes, void* out, float* lse,
+                       int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -261,10 +261,16 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t 
   return prefill_ws_bytes(batch, dims->n_heads, max_blocks);
 }
 
-int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv,
-                const void* cache, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
-                const int32_t* seq_lens, int32_t batch, int32_t t, float softmax_scale, void* workspace,
-                size_t workspace_bytes, void* out, float* lse, int32_t* status, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kPrefillExpand = 1, kPrefillAttend = 2;
+
+int prefill_phases(int phases, const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
+                   const void* w_uv, const void* cache, int32_t num_blocks, const int32_t* block_table,
+                   int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t t, float softmax_scale,
+                   void* workspace, size_t workspace_bytes, void* out, float* lse, int32_t* status, void* stream) {
   int rc = check_dims(dims);
   if (rc != MLA_OK) return rc;
   if (dims->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
@@ -292,13 +298,32 @@ int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope, co
   hipStream_t st = (hipStream_t)stream;
   uint16_t* kc = (uint16_t*)workspace;
   uint16_t* vt = kc + need / 4;   // the second half: V^T
-  hipError_t e = launch_expand_kv_bf16((const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch,
-                                       dims->n_heads, (const uint16_t*)w_uk, (const uint16_t*)w_uv, kc, vt, status, st);
-  if (e == hipSuccess)
+  hipError_t e = hipSuccess;
+  if (phases & kPrefillExpand)
+    e = launch_expand_kv_bf16((const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch,
+                              dims->n_heads, (const uint16_t*)w_uk, (const uint16_t*)w_uv, kc, vt, status, st);
+  if (e == hipSuccess && (phases & kPrefillAttend))
     e = launch_prefill_attn_bf16((const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)cache,
                                  num_blocks, block_table, max_blocks, seq_lens, batch, t, dims->n_heads,
                                  softmax_scale, kc, vt, (uint16_t*)out, lse, status, st);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+}  // namespace
+
+#define MLA_PREFILL_PARAMS                                                                                     \
+  const mla_dims *dims, const void *q_nope, const void *q_rope, const void *w_uk, const void *w_uv,              \
+      const void *cache, int32_t num_blocks, const int32_t *block_table, int32_t max_blocks,                     \
+      const int32_t *seq_lens, int32_t batch, int32_t t, float softmax_scale, void *workspace,                   \
+      size_t workspace_bytes, void *out, float *lse, int32_t *status, void *stream
+#define MLA_PREFILL_ARGS                                                                                          \
+  dims, q_nope, q_rope, w_uk, w_uv, cache, num_blocks, block_table, max_blocks, seq_lens, batch, t, softmax_scale, \
+      workspace, workspace_bytes, out, lse, status, stream
+
+extern "C" {
+
+int mla_prefill(MLA_PREFILL_PARAMS) { return prefill_phases(kPrefillExpand | kPrefillAttend, MLA_PREFILL_ARGS); }
+int mla_prefill_expand(MLA_PREFILL_PARAMS) { return prefill_phases(kPrefillExpand, MLA_PREFILL_ARGS); }
+int mla_prefill_attend(MLA_PREFILL_PARAMS) { return prefill_phases(kPrefillAttend, MLA_PREFILL_ARGS); }
 
 }  // extern "C"

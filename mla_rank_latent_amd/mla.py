@@ -23,7 +23,8 @@ MLA_STATUS_BAD_POS = 0x4
 
 EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_append_workspace_bytes",
            "mla_q_project", "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
-           "mla_decode_finish", "mla_prefill_workspace_bytes", "mla_prefill")
+           "mla_decode_finish", "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_expand",
+           "mla_prefill_attend")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or python -m mla_rank_latent_amd.build)")
@@ -64,9 +65,10 @@ _lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I, _I]
 _lib.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
 _lib.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I]
-_lib.mla_prefill.restype = ctypes.c_int
-_lib.mla_prefill.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P,
-                             ctypes.c_size_t, _P, _P, _P, _P]
+for _name in ("mla_prefill", "mla_prefill_expand", "mla_prefill_attend"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
+                                     ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P, _P]
 for _name in ("mla_decode", "mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
@@ -170,11 +172,25 @@ def mla_prefill(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_
     q_rope [batch, t, n_heads, d_rope] (rotated); out [batch, t, n_heads, d_nope] and optional lse
     [batch, t, n_heads] float32 written.  ``workspace`` is a byte tensor of at least
     mla_prefill_workspace_bytes(d, batch, max_blocks)."""
+    prepared_prefill("mla_prefill", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
+                     workspace, out, lse=lse, status=status, stream=stream)()
+
+
+def prepared_prefill(fn_name: str, d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens,
+                     softmax_scale: float, workspace, out, lse=None, status=None, stream=None):
+    """Marshal the arguments of ``fn_name`` (mla_prefill or one of its phases, mla_prefill_expand and
+    mla_prefill_attend) once and return a zero-argument launcher; every launch still checks the return code."""
+    if fn_name not in ("mla_prefill", "mla_prefill_expand", "mla_prefill_attend"):
+        raise ValueError(fn_name)
     batch, t = int(q_nope.shape[0]), int(q_nope.shape[1])
-    _check("mla_prefill", _lib.mla_prefill(
-        ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
-        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, t, float(softmax_scale),
-        _ptr(workspace), _nbytes(workspace), _ptr(out), _ptr(lse), _ptr(status), _stream(stream)))
+    fn = getattr(_lib, fn_name)
+    args = (ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
+            _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, t, float(softmax_scale),
+            _ptr(workspace), _nbytes(workspace), _ptr(out), _ptr(lse), _ptr(status), _stream(stream))
+
+    def launch() -> None:
+        _check(fn_name, fn(*args))
+    return launch
 
 
 def mla_decode_prepare(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,

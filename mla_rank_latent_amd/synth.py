@@ -115,6 +115,14 @@ def _weight(rng, out_f: int, in_f: int, dtype: str) -> np.ndarray:
     return _normals(rng, out_f * in_f, 1.0 / math.sqrt(in_f), dtype).reshape(out_f, in_f)
 
 
+def prefill_presets() -> Dict[str, Spec]:
+    """Prefill workloads: every one of the sequence's tokens is appended from hidden states and is a query."""
+    return {
+        "prefill_b1_ctx8192": Spec("prefill_b1_ctx8192", batch=1, sq=8192, seed=6, seq_lens=[8192], paged=True,
+                                   append=True),
+    }
+
+
 def make_inputs(spec: Spec) -> Dict[str, object]:
     """Draw every input of ``spec``.  bf16 arrays are uint16 bit patterns."""
     rng = np.random.default_rng(spec.seed)

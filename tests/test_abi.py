@@ -103,6 +103,41 @@ def test_decode_argument_errors():
     assert _decode(mla.dims(8, 16, 8, 2048, 64, dtype="f32")) == -6
 
 
+def _prefill(d, fn="mla_prefill", **kw):
+    a = dict(q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE, cache=FAKE, num_blocks=16, block_table=FAKE,
+             max_blocks=4, seq_lens=FAKE, batch=2, t=100, scale=0.1, ws=FAKE, ws_bytes=1 << 40,
+             out=FAKE, lse=None, status=None, stream=None)
+    a.update(kw)
+    return getattr(mla.raw_library(), fn)(
+        ctypes.byref(d), a["q_nope"], a["q_rope"], a["w_uk"], a["w_uv"], a["cache"], a["num_blocks"],
+        a["block_table"], a["max_blocks"], a["seq_lens"], a["batch"], a["t"], a["scale"], a["ws"], a["ws_bytes"],
+        a["out"], a["lse"], a["status"], a["stream"])
+
+
+def test_prefill_workspace_and_argument_errors():
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    # K^C and V^T of every token slot: 2 x batch x heads x (max_blocks x 64) x 128 bf16
+    assert mla.mla_prefill_workspace_bytes(v2, 2, 4) == 2 * 2 * 128 * 256 * 128 * 2
+    assert mla.mla_prefill_workspace_bytes(v2, 0, 4) == 0
+    assert mla.mla_prefill_workspace_bytes(v2, 2, 0) == 0
+    assert mla.mla_prefill_workspace_bytes(v2, 1, (1 << 17) + 1) == 0          # past 2^23 token slots
+    assert mla.mla_prefill_workspace_bytes(mla.dims(8, 16, 8, 32, 64, dtype="f32"), 2, 4) == 0
+    need = mla.mla_prefill_workspace_bytes(v2, 2, 4)
+    for fn in ("mla_prefill", "mla_prefill_expand", "mla_prefill_attend"):
+        assert _prefill(v2, fn, q_rope=None) == -1
+        assert _prefill(v2, fn, ws=None) == -1
+        assert _prefill(v2, fn, t=0) == -2
+        assert _prefill(v2, fn, t=257) == -2                  # more queries than token slots
+        assert _prefill(v2, fn, scale=float("inf")) == -2
+        assert _prefill(v2, fn, batch=0) == -2
+        assert _prefill(v2, fn, out=FAKE + 4) == -4
+        assert _prefill(v2, fn, ws=FAKE + 128) == -4
+        assert _prefill(v2, fn, ws_bytes=need - 1) == -5
+        assert _prefill(v2, fn, max_blocks=(1 << 17) + 1, num_blocks=1 << 18) == -6
+        assert _prefill(mla.dims(8, 16, 8, 32, 64, dtype="f32"), fn) == -8
+        assert _prefill(mla.dims(128, 128, 64, 512, 5120, block_size=32), fn) == -8
+
+
 def test_append_and_qproj_argument_errors():
     lib = mla.raw_library()
     v2 = mla.dims(128, 128, 64, 512, 5120)
