@@ -249,8 +249,8 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t 
  *
  * q_nope     [batch, t, n_heads, d_nope]   bf16
  * q_rope     [batch, t, n_heads, d_rope]   bf16, already rotated
- * w_uk, w_uv, cache, block_table, seq_lens, softmax_scale, lse, status: as for
- *            mla_decode
+ * w_uk, w_uv, cache, block_table, seq_lens, lse, status: as for mla_decode
+ * softmax_scale  positive and finite (MLA_ERR_BAD_DIMS otherwise)
  * t          query tokens per sequence, 1 .. max_blocks * block_size
  * workspace  device scratch of at least mla_prefill_workspace_bytes(dims,
  *            batch, max_blocks) bytes, 256-byte aligned; clobbered

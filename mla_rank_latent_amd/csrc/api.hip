@@ -278,7 +278,8 @@ int prefill_phases(int phases, const mla_dims* dims, const void* q_nope, const v
     return MLA_ERR_NULL_PTR;
   if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
   if ((long long)max_blocks * dims->block_size > (1ll << 23)) return MLA_ERR_CAPACITY;
-  if (t < 1 || (long long)t > (long long)max_blocks * dims->block_size || !std::isfinite(softmax_scale))
+  if (t < 1 || (long long)t > (long long)max_blocks * dims->block_size || !std::isfinite(softmax_scale) ||
+      !(softmax_scale > 0.0f))
     return MLA_ERR_BAD_DIMS;
   if ((long long)batch * t * dims->n_heads >= (1ll << 31)) return MLA_ERR_CAPACITY;
   {

@@ -376,28 +376,34 @@ __global__ __launch_bounds__(512) void prefill_attn_bf16_kernel(
     }
 
     // ---- softmax.  Lane holds row n, tokens 64 kt + 32 i + 8 (r / 4) + 4 g + r % 4.
-    float z[2][16];
-    const bool mask = kt * kFKT + kFKT - 1 > pos_first;
+    // The maximum is taken on the raw scores (the scale is positive) and the scale
+    // enters the exponent's fma, so z = scale * s is never formed on its own.
+    f32x16* sv = acc_s;   // masked in place
+    if (kt * kFKT + kFKT - 1 > pos_first) {
+      // a diagonal tile (some key follows some row of this wave): token offset
+      // 32 i + 8 (r / 4) + r % 4 is masked when it exceeds thr.  The empty asm keeps
+      // this a branch: if-converted, its selects would run on every tile.
+      asm volatile("");
+      const int thr = pos - kt * kFKT - 4 * g;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sv[i][r] = (32 * i + 8 * (r >> 2) + (r & 3) > thr) ? -__builtin_inff() : sv[i][r];
+    }
+    float mt = sv[0][0];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = kt * kFKT + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float v = acc_s[i][r] * scale_log2;
-        z[i][r] = (mask && tok > pos) ? -__builtin_inff() : v;
-      }
-    float mt = z[0][0];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, z[i][r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[i][r]);
     {
       // lanes l and l ^ 32 hold the two token halves of row n
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
     }
     const bool resc = mt > m_ref + kFTau;   // false while the row has seen only masked keys
     if (__builtin_amdgcn_ballot_w64(resc) != 0ull) {
+      asm volatile("");   // a branch, not 64 multiplies by 1 on every tile
       const float f = resc ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.0f;   // 0 on the first finite tile
       l_sum *= f;
 #pragma unroll
@@ -406,18 +412,24 @@ __global__ __launch_bounds__(512) void prefill_attn_bf16_kernel(
         for (int r = 0; r < 16; ++r) acc_o[i][r] *= f;
       m_ref = resc ? mt : m_ref;
     }
-    const float msafe = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+    const float neg_m = m_ref == -__builtin_inff() ? 0.0f : -m_ref;
     u32x4 pk[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int i = kk >> 1, hb = 8 * (kk & 1);
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(z[i][hb + e] - msafe);
-        l_sum += p[e];
-      }
-      pk[kk] = u32x4{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7])};
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i][hb + e], scale_log2, neg_m));
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf2(p[2 * e], p[2 * e + 1]);
+      // the weight sum of the rounded weights the value product uses, two per dot2
+      // (from the packed words themselves, not from elements of the vector below)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
+                                                __builtin_bit_cast(bf16x2, 0x3f803f80u), l_sum, false);
+      pk[kk] = u32x4{w[0], w[1], w[2], w[3]};
     }
 
     // ---- O^T += V^T . P^T: 4 feature tiles x 4 token k-steps

@@ -129,6 +129,8 @@ def test_prefill_workspace_and_argument_errors():
         assert _prefill(v2, fn, t=0) == -2
         assert _prefill(v2, fn, t=257) == -2                  # more queries than token slots
         assert _prefill(v2, fn, scale=float("inf")) == -2
+        assert _prefill(v2, fn, scale=0.0) == -2
+        assert _prefill(v2, fn, scale=-0.1) == -2
         assert _prefill(v2, fn, batch=0) == -2
         assert _prefill(v2, fn, out=FAKE + 4) == -4
         assert _prefill(v2, fn, ws=FAKE + 128) == -4
