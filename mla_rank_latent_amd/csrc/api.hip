@@ -283,10 +283,12 @@ int prefill_phases(int phases, const mla_dims* dims, const void* q_nope, const v
     return MLA_ERR_BAD_DIMS;
   if ((long long)batch * t * dims->n_heads >= (1ll << 31)) return MLA_ERR_CAPACITY;
   {
-    // launch grids: (sequence, 128-token tile, head) and (sequence x head rounded to 8, 256-row query tile)
+    // launch grids: expansion (8 XCDs x head sets x token-tile groups x 32) and attention
+    // ((sequence x head) rounded to 8, x 256-row query tiles)
     const long long tiles = ((long long)max_blocks * dims->block_size + 127) / 128;
     const long long qtiles = ((long long)t + 255) / 256;
-    if ((long long)batch * tiles * dims->n_heads >= (1ll << 31) ||
+    const long long xgrid = 8 * (((dims->n_heads + 7) / 8 + 3) / 4) * (((long long)batch * tiles + 7) / 8) * 32;
+    if (xgrid >= (1ll << 31) ||
         ((long long)batch * dims->n_heads + 7) / 8 * 8 * qtiles >= (1ll << 31))
       return MLA_ERR_CAPACITY;
   }

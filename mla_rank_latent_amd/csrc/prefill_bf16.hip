@@ -84,15 +84,20 @@ __device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1)
 
 // ---- expansion ---------------------------------------------------------------
 constexpr int kXTok = 128;                        // tokens per workgroup
-constexpr int kXK = 64;                           // latent features per chunk
-constexpr int kXRegion = 128 * kXK * 2;           // 16 KB: 128 rows of 128 B
+constexpr int kXK = 32;                           // latent features per chunk
+constexpr int kXRow = kXK * 2;                    // 64 B per row and chunk
+constexpr int kXRegion = 128 * kXRow;             // 8 KB: 128 rows
 constexpr int kXChunk = 3 * kXRegion;             // latent rows, W^UK_h rows, W^UV_h rows
-constexpr int kXCopies = kXChunk / 1024 / 4;      // 1 KB copies per wave per chunk (12)
-constexpr int kXChunks = kLat / kXK;              // 8
+constexpr int kXCopies = kXChunk / 1024 / 4;      // 1 KB copies per wave per chunk (6)
+constexpr int kXChunks = kLat / kXK;              // 16
+constexpr int kXStages = 3;                       // LDS ring depth: two chunks in flight (72 KB,
+                                                  // so two workgroups fit on a CU)
 
 // LDS rows of 128 B: 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so the
 // 16 rows read by 16 lanes at one logical chunk cover all banks
 __device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
+// LDS rows of 64 B: chunk c of row r at c ^ ((r >> 2) & 3), for the same reason
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
 
 // ---- attention -----------------------------------------------------------------
 constexpr int kFWaves = 8;
@@ -108,19 +113,29 @@ constexpr float kFTau = 8.0f;                     // lazy-rescale threshold (log
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void expand_kv_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void expand_kv_bf16_kernel(
     const uint16_t* __restrict__ cache, int num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
-    const int32_t* __restrict__ seq_lens, int n_heads, int t_ctx, int n_tiles, const uint16_t* __restrict__ w_uk,
+    const int32_t* __restrict__ seq_lens, int batch, int n_heads, int t_ctx, int n_tiles,
+    const uint16_t* __restrict__ w_uk,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
     int32_t* __restrict__ status) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kXChunk];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kXStages * kXChunk];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
 
-  // heads fastest: consecutive workgroups (one per XCD in turn) share the latent tile
-  const int h = blockIdx.x % n_heads;
-  const int rest = blockIdx.x / n_heads;
-  const int tile = rest % n_tiles;
-  const int b = rest / n_tiles;
+  // Workgroup i runs on XCD x = i % 8 (the i / 8-th there).  Each XCD takes the
+  // heads h = x mod 8 and works through sets of 4 of its heads x 8 token tiles,
+  // so that the 32 workgroups it holds at a time share 4 heads' weights and 8
+  // latent tiles (about 2 MB) in its L2.
+  const int x = blockIdx.x & 7;
+  const int jx = blockIdx.x >> 3;
+  const int n_bt = batch * n_tiles;
+  const int n_tg = (n_bt + 7) / 8;
+  const int inner = jx & 31, outer = jx >> 5;
+  const int h = x + 8 * (4 * (outer / n_tg) + (inner >> 3));
+  const int bt = 8 * (outer % n_tg) + (inner & 7);
+  if (h >= n_heads || bt >= n_bt) return;
+  const int tile = bt % n_tiles;
+  const int b = bt / n_tiles;
   int L = seq_lens[b];
   L = L < 0 ? 0 : (L > t_ctx ? t_ctx : L);
   const int t0 = tile * kXTok;
@@ -132,16 +147,16 @@ __global__ __launch_bounds__(256) void expand_kv_bf16_kernel(
   const int g = lane >> 5;
   const int n = lane & 31;
 
-  // copy plan: copy q (0..47) of a chunk moves region q / 16, rows 8 (q % 16) .. +7;
-  // lane i lands at row 8 (q % 16) + i / 8, physical chunk i % 8, and fetches the
-  // logical chunk (i % 8) ^ swz128(row).  Wave w issues copies w + 4 k.
+  // copy plan: copy q (0..23) of a chunk moves region q / 8, rows 16 (q % 8) .. +15;
+  // lane i lands at row 16 (q % 8) + i / 4, physical chunk i % 4, and fetches the
+  // logical chunk (i % 4) ^ swz64(row).  Wave w issues copies w + 4 k.
   uint64_t src[kXCopies];
 #pragma unroll
   for (int k = 0; k < kXCopies; ++k) {
     const int q = wave + 4 * k;
-    const int region = q / 16;
-    const int r = 8 * (q % 16) + lane / 8;
-    const int lc = (lane % 8) ^ swz128(r);
+    const int region = q / 8;
+    const int r = 16 * (q % 8) + lane / 4;
+    const int lc = (lane % 4) ^ swz64(r);
     const uint8_t* rowp;
     if (region == 0) {
       int t = t0 + r;
@@ -156,10 +171,10 @@ __global__ __launch_bounds__(256) void expand_kv_bf16_kernel(
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   auto issue = [&](int ch) {
-    const uint32_t dst = lds0 + (ch & 1) * kXChunk;
+    const uint32_t dst = lds0 + (ch % kXStages) * kXChunk;
 #pragma unroll
     for (int k = 0; k < kXCopies; ++k)
-      dma16_v(src[k] + (uint64_t)ch * (kXK * 2), __builtin_amdgcn_readfirstlane(dst + (wave + 4 * k) * 1024));
+      dma16_v(src[k] + (uint64_t)ch * kXRow, __builtin_amdgcn_readfirstlane(dst + (wave + 4 * k) * 1024));
   };
 
   const int tq = wave >> 1;    // token quadrant: tokens 64 tq .. +63
@@ -173,15 +188,14 @@ __global__ __launch_bounds__(256) void expand_kv_bf16_kernel(
       for (int r = 0; r < 16; ++r) acck[i][j][r] = accv[i][j][r] = 0.0f;
 
   issue(0);
+  issue(1);
   for (int ch = 0; ch < kXChunks; ++ch) {
-    if (ch + 1 < kXChunks) {
-      issue(ch + 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kXCopies));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    __syncthreads();   // chunk ch visible to every wave
-    const MLA_LDS uint8_t* buf = lds + (ch & 1) * kXChunk;
+    // chunk ch has landed once at most chunk ch + 1's copies are in flight
+    if (ch + 1 < kXChunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kXCopies));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();   // chunk ch visible to every wave; chunk ch - 1's buffer free
+    if (ch + 2 < kXChunks) issue(ch + 2);
+    const MLA_LDS uint8_t* buf = lds + (ch % kXStages) * kXChunk;
 #pragma unroll
     for (int ks = 0; ks < kXK / 16; ++ks) {
       const int lc = 2 * ks + g;
@@ -190,9 +204,9 @@ __global__ __launch_bounds__(256) void expand_kv_bf16_kernel(
       for (int i = 0; i < 2; ++i) {
         const int rc = 64 * tq + 32 * i + n;
         const int rw = 64 * dq + 32 * i + n;
-        cop[i] = lds16(buf + rc * 128 + ((lc ^ swz128(rc)) << 4));
-        kop[i] = lds16(buf + kXRegion + rw * 128 + ((lc ^ swz128(rw)) << 4));
-        vop[i] = lds16(buf + 2 * kXRegion + rw * 128 + ((lc ^ swz128(rw)) << 4));
+        cop[i] = lds16(buf + rc * kXRow + ((lc ^ swz64(rc)) << 4));
+        kop[i] = lds16(buf + kXRegion + rw * kXRow + ((lc ^ swz64(rw)) << 4));
+        vop[i] = lds16(buf + 2 * kXRegion + rw * kXRow + ((lc ^ swz64(rw)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -202,37 +216,51 @@ __global__ __launch_bounds__(256) void expand_kv_bf16_kernel(
           accv[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(cop[i]), as_bf8(vop[j]), accv[i][j], 0, 0, 0);
         }
     }
-    __syncthreads();   // every wave done with this buffer before chunk ch + 2 lands in it
   }
 
-  // D layout of 32x32x16: register r holds row 8 (r / 4) + 4 g + r % 4, column n.
-  // With an odd max_blocks the last tile reaches 64 slots past t_ctx: those are not stored.
-  const size_t bh = (size_t)b * n_heads + h;
-  uint16_t* kc_bh = kc + bh * t_ctx * kNope;
-  uint16_t* vt_bh = vt + bh * kNope * (size_t)t_ctx;
+  // D layout of 32x32x16: register r holds row 8 (r / 4) + 4 g + r % 4, column n,
+  // so each lane holds 4 consecutive elements of a stored row per (tile, r / 4).
+  // Both 128 x 128 result tiles are staged in LDS (rows of 256 B, 16-byte chunk c
+  // of row x at c ^ (x & 15)) and written out as whole rows, 16 bytes per lane.
+  __syncthreads();   // every wave done with the last chunk
+  MLA_LDS uint8_t* sk = lds;                  // K^C tile: row = token, 128 features
+  MLA_LDS uint8_t* sv = lds + 128 * 256;      // V^T tile: row = feature, 128 stored token slots
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // K^C^T tile (d tile i, token tile j): 4 consecutive d of token row
         {
-          const int d = 64 * dq + 32 * i + 8 * q + 4 * g;
-          const int tok = t0 + 64 * tq + 32 * j + n;
+          const int d = 64 * dq + 32 * i + 8 * q + 4 * g;     // 4 consecutive features
+          const int tok = 64 * tq + 32 * j + n;
           const u32x2 v = {pack_bf2(acck[i][j][4 * q], acck[i][j][4 * q + 1]),
                            pack_bf2(acck[i][j][4 * q + 2], acck[i][j][4 * q + 3])};
-          if (tok < t_ctx) *(u32x2*)(kc_bh + (size_t)tok * kNope + d) = v;
+          *(MLA_LDS u32x2*)(sk + tok * 256 + (((d >> 3) ^ (tok & 15)) << 4) + (d & 4) * 2) = v;
         }
-        // V tile (token tile i, d tile j): 4 consecutive tokens of feature row d
         {
-          const int tok = t0 + 64 * tq + 32 * i + 8 * q + 4 * g;
+          const int tok = vt_pos(64 * tq + 32 * i + 8 * q + 4 * g);   // 4 consecutive tokens
           const int d = 64 * dq + 32 * j + n;
           const u32x2 v = {pack_bf2(accv[i][j][4 * q], accv[i][j][4 * q + 1]),
                            pack_bf2(accv[i][j][4 * q + 2], accv[i][j][4 * q + 3])};
-          if (tok < t_ctx) *(u32x2*)(vt_bh + (size_t)d * t_ctx + vt_pos(tok)) = v;
+          *(MLA_LDS u32x2*)(sv + d * 256 + (((tok >> 3) ^ (d & 15)) << 4) + (tok & 4) * 2) = v;
         }
       }
+  __syncthreads();
+  const size_t bh = (size_t)b * n_heads + h;
+  uint16_t* kc_bh = kc + bh * t_ctx * kNope;
+  uint16_t* vt_bh = vt + bh * kNope * (size_t)t_ctx;
+  // 128 rows x 16 chunks per tile; thread tid takes chunk tid % 16 of rows tid / 16 + 16 k.
+  // With an odd max_blocks the tile reaches 64 slots past t_ctx: those are not stored.
+  const int c = tid & 15;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int x = (tid >> 4) + 16 * k;
+    const u32x4 vk = lds16(sk + x * 256 + ((c ^ (x & 15)) << 4));
+    if (t0 + x < t_ctx) *(u32x4*)(kc_bh + (size_t)(t0 + x) * kNope + 8 * c) = vk;
+    const u32x4 vv = lds16(sv + x * 256 + ((c ^ (x & 15)) << 4));
+    if (t0 + 8 * c < t_ctx) *(u32x4*)(vt_bh + (size_t)x * t_ctx + t0 + 8 * c) = vv;
+  }
 }
 
 __global__ __launch_bounds__(512) void prefill_attn_bf16_kernel(
@@ -482,9 +510,12 @@ hipError_t launch_expand_kv_bf16(const uint16_t* cache, int num_blocks, const in
                                  const uint16_t* w_uv, uint16_t* kc, uint16_t* vt, int32_t* status, hipStream_t st) {
   const int t_ctx = max_blocks * kBlk;
   const int n_tiles = (t_ctx + kXTok - 1) / kXTok;
-  dim3 grid((unsigned)((size_t)batch * n_tiles * n_heads));
+  // 8 XCDs x (head sets of 4 per XCD) x (groups of 8 token tiles) x 32
+  const long long n_tg = ((long long)batch * n_tiles + 7) / 8;
+  const long long n_hs = ((n_heads + 7) / 8 + 3) / 4;
+  dim3 grid((unsigned)(8 * n_hs * n_tg * 32));
   hipLaunchKernelGGL(expand_kv_bf16_kernel, grid, dim3(256), 0, st, cache, num_blocks, block_table, max_blocks,
-                     seq_lens, n_heads, t_ctx, n_tiles, w_uk, w_uv, kc, vt, status);
+                     seq_lens, batch, n_heads, t_ctx, n_tiles, w_uk, w_uv, kc, vt, status);
   return hipGetLastError();
 }
 
