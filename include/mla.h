@@ -121,9 +121,12 @@ size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens);
  *            With it (bf16) the products are split over the d_model axis across
  *            many workgroups and summed in a fixed order by a second kernel, so
  *            the weights stream at memory rate; NULL (with workspace_bytes 0)
- *            runs one kernel that needs no scratch.  Either way the result does
- *            not depend on timing; the two paths may differ in the last bit,
- *            because they sum in different orders.
+ *            runs one kernel that needs no scratch.  From 2048 rows (batch*t)
+ *            with d_model a multiple of 64 (bf16), a third path runs: one GEMM
+ *            kernel over the whole d_model per tile, which needs no scratch and
+ *            ignores the workspace (mla_cache_append_workspace_bytes returns 0
+ *            there).  Every path's result is independent of timing; paths may
+ *            differ in the last bit, because they sum in different orders.
  * status     optional int32 (device), OR-ed with MLA_STATUS_BAD_POS/BAD_BLOCK; a
  *            row whose position or block is invalid is skipped.
  */

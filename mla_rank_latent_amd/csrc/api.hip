@@ -134,9 +134,15 @@ size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens) {
   return (size_t)tokens * ((size_t)dims->d_latent + dims->d_rope) * elem_size(dims->dtype);
 }
 
+namespace {
+bool append_uses_gemm(const mla_dims* d, long long tokens) {
+  return d->dtype == MLA_DTYPE_BF16 && tokens >= kAppendGemmMinTokens && d->d_model % 64 == 0;
+}
+}  // namespace
+
 size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t t) {
   if (check_dims(dims) != MLA_OK || batch < 1 || t < 1 || (long long)batch * t >= (1ll << 30)) return 0;
-  if (dims->dtype != MLA_DTYPE_BF16) return 0;
+  if (dims->dtype != MLA_DTYPE_BF16 || append_uses_gemm(dims, (long long)batch * t)) return 0;
   return append_split_ws_bytes(dims->d_model, (long long)batch * t);
 }
 
@@ -152,12 +158,17 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
   if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(positions) || !aligned16(block_table) ||
       !aligned16(cache) || (status && ((uintptr_t)status & 3u)) || (workspace && !aligned16(workspace)))
     return MLA_ERR_BAD_ALIGN;
-  const bool split = workspace != nullptr && dims->dtype == MLA_DTYPE_BF16;
+  const bool gemm = append_uses_gemm(dims, (long long)batch * t);
+  const bool split = !gemm && workspace != nullptr && dims->dtype == MLA_DTYPE_BF16;
   if (split && workspace_bytes < append_split_ws_bytes(dims->d_model, (long long)batch * t))
     return MLA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (split)
+  if (gemm)
+    e = launch_append_gemm_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions,
+                                block_table, max_blocks, (uint16_t*)cache, num_blocks, batch * t, t, dims->d_model,
+                                dims->rope_base, status, st);
+  else if (split)
     e = launch_append_split_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions,
                                  block_table, max_blocks, (uint16_t*)cache, num_blocks, batch * t, t, dims->d_model,
                                  dims->rope_base, (float*)workspace, status, st);

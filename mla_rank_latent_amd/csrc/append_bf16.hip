@@ -236,6 +236,164 @@ __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __
   *(uint32_t*)(cache + ((size_t)blk * kBlk + pos % kBlk) * kRow + col) = outv;
 }
 
+// ---------------------------------------------------------------------------
+// Many-token path (prefill chunks): a plain GEMM [tokens x d] . [d x 576] over
+// the whole d_model per workgroup, no scratch.  Workgroup = (128 tokens, 192
+// columns); the h rows and weight rows stream through a 3-slot LDS ring in
+// 64-feature chunks (direct-to-LDS copies, 1 KB each; 16-byte chunk c of a
+// 128-byte LDS row r at c ^ ((r >> 1) & 7)).  Wave (tm, tn) accumulates tokens
+// 64 tm .. +63 x columns 96 tn .. +95 on MFMA 32x32x16.  The fp32 tile is then
+// staged in LDS and written as bf16 rows, the k^R pairs turned in fp64 first.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kGM = 128;                      // tokens per workgroup
+constexpr int kGN = 192;                      // columns per workgroup (576 = 3 x 192)
+constexpr int kGK = 64;                       // d_model features per chunk
+constexpr int kGChunk = (kGM + kGN) * kGK * 2;   // 40 KB
+constexpr int kGCopies = kGChunk / 1024 / 4;     // 10 copies of 1 KB per wave and chunk
+constexpr int kGStages = 3;
+
+__device__ __forceinline__ void dma16_row(uint64_t addr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
+}  // namespace
+
+__global__ __launch_bounds__(256) void append_gemm_bf16_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv, const uint16_t* __restrict__ w_kr,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ block_table, int max_blocks,
+    uint16_t* __restrict__ cache, int num_blocks, int tokens, int t_per_seq, int d_model, double rope_base,
+    int32_t* status) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGStages * kGChunk];
+  MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
+  const int tn = blockIdx.x % (kRow / kGN);   // the 3 column tiles of a token tile run side by side
+  const int m0 = (blockIdx.x / (kRow / kGN)) * kGM;
+  const int n0 = tn * kGN;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int n = lane & 31;
+
+  // copy q (0..39) of a chunk: rows 8 q .. 8 q + 7 of the (h rows, weight rows)
+  // stack; wave w issues copies w + 4 k.  Lane i: row 8 q + i / 8, physical chunk
+  // i % 8, logical chunk (i % 8) ^ gswz(row).
+  uint64_t src[kGCopies];
+#pragma unroll
+  for (int k = 0; k < kGCopies; ++k) {
+    const int r = 8 * (wave + 4 * k) + lane / 8;
+    const int lc = (lane % 8) ^ gswz(r);
+    const uint16_t* rowp;
+    if (r < kGM) {
+      const int t = m0 + r < tokens ? m0 + r : tokens - 1;
+      rowp = h + (size_t)t * d_model;
+    } else {
+      const int c = n0 + r - kGM;
+      rowp = c < kLat ? w_dkv + (size_t)c * d_model : w_kr + (size_t)(c - kLat) * d_model;
+    }
+    src[k] = (uint64_t)(uintptr_t)(rowp + 8 * lc);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue = [&](int ch) {
+    const uint32_t dst = lds0 + (ch % kGStages) * kGChunk;
+#pragma unroll
+    for (int k = 0; k < kGCopies; ++k)
+      dma16_row(src[k] + (uint64_t)ch * (kGK * 2), __builtin_amdgcn_readfirstlane(dst + (wave + 4 * k) * 1024));
+  };
+
+  const int tm = wave >> 1, tw = wave & 1;
+  f32x16 acc[2][3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nch = d_model / kGK;
+  issue(0);
+  if (nch > 1) issue(1);
+  for (int ch = 0; ch < nch; ++ch) {
+    if (ch + 1 < nch) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kGCopies));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();   // chunk ch visible to every wave; chunk ch - 1's slot free
+    if (ch + 2 < nch) issue(ch + 2);
+    const MLA_LDS uint8_t* buf = lds + (ch % kGStages) * kGChunk;
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      const int lc = 2 * ks + g;
+      u32x4 a[2], b[3];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * tm + 32 * i + n;
+        a[i] = *(const MLA_LDS u32x4*)(buf + r * 128 + ((lc ^ gswz(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int r = kGM + 96 * tw + 32 * j + n;
+        b[j] = *(const MLA_LDS u32x4*)(buf + r * 128 + ((lc ^ gswz(r)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a[i]), as_bf8(b[j]), acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- stage the fp32 tile [128 tokens][192 columns] (96 KB) and write the rows
+  __syncthreads();   // every wave done with the last chunk
+  MLA_LDS float* tile = (MLA_LDS float*)lds;
+  // D layout: register r holds token row 8 (r / 4) + 4 g + r % 4, column n
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tile[(64 * tm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3)) * kGN + 96 * tw + 32 * j + n] = acc[i][j][r];
+  __syncthreads();
+  // thread = (token, pair of adjacent columns): 128 x 96 pairs; a k^R pair is one RoPE pair
+  for (int idx = tid; idx < kGM * (kGN / 2); idx += 256) {
+    const int row = idx / (kGN / 2);
+    const int cp = 2 * (idx % (kGN / 2));
+    const int tok = m0 + row;
+    if (tok >= tokens) continue;
+    const float v0 = tile[row * kGN + cp], v1 = tile[row * kGN + cp + 1];
+    const int col = n0 + cp;
+    const int b = tok / t_per_seq;
+    const int pos = positions[tok];
+    if (pos < 0 || pos >= max_blocks * kBlk) {
+      if (status) atomicOr(status, MLA_STATUS_BAD_POS);
+      continue;
+    }
+    const int blk = block_table[(size_t)b * max_blocks + pos / kBlk];
+    if (blk < 0 || blk >= num_blocks) {
+      if (status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
+      continue;
+    }
+    uint32_t outv;
+    if (col < kLat) {
+      outv = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+    } else {
+      double y0, y1;
+      rope_pair((double)v0, (double)v1, pos, (col - kLat) >> 1, kRope, rope_base, &y0, &y1);
+      outv = (uint32_t)d2bf(y0) | ((uint32_t)d2bf(y1) << 16);
+    }
+    *(uint32_t*)(cache + ((size_t)blk * kBlk + pos % kBlk) * kRow + col) = outv;
+  }
+}
+
+hipError_t launch_append_gemm_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
+                                   const int32_t* positions, const int32_t* block_table, int max_blocks,
+                                   uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
+                                   float rope_base, int32_t* status, hipStream_t st) {
+  dim3 grid((unsigned)(((long long)tokens + kGM - 1) / kGM * (kRow / kGN)));
+  hipLaunchKernelGGL(append_gemm_bf16_kernel, grid, dim3(256), 0, st, h, w_dkv, w_kr, positions, block_table,
+                     max_blocks, cache, num_blocks, tokens, t_per_seq, d_model, (double)rope_base, status);
+  return hipGetLastError();
+}
+
 int append_split_slices(int d_model) {
   const int nks = d_model / 32;
   return (nks + kSliceSteps - 1) / kSliceSteps;

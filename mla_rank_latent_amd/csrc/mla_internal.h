@@ -85,6 +85,13 @@ hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_bl
                             hipStream_t st);
 hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads,
                                  uint8_t* ws, uint16_t* out, float* lse, hipStream_t st);
+// many-token append (prefill chunks): one GEMM kernel, no workspace; used for bf16 when
+// batch * t >= kAppendGemmMinTokens and d_model is a multiple of 64
+constexpr int kAppendGemmMinTokens = 2048;
+hipError_t launch_append_gemm_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
+                                   const int32_t* positions, const int32_t* block_table, int max_blocks,
+                                   uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
+                                   float rope_base, int32_t* status, hipStream_t st);
 // prefill (expanded form): workspace bytes, K^C / V^T expansion, causal attention
 size_t prefill_ws_bytes(int batch, int n_heads, int max_blocks);
 hipError_t launch_expand_kv_bf16(const uint16_t* cache, int num_blocks, const int32_t* block_table, int max_blocks,

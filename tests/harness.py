@@ -74,9 +74,10 @@ class GpuCase:
         self.out = torch.empty(B, S, H, spec.d_nope, dtype=tdt, device="cuda")
         self.lse = torch.empty(B, S, H, dtype=torch.float32, device="cuda")
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        # decode's workspace (none for query groups decode does not take, e.g. a
+        # many-token append case that only appends)
         nbytes = mla.mla_decode_workspace_bytes(self.d, B, S, num_splits)
-        assert nbytes > 0
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes > 0 else None
 
     def append(self, split=True):
         """split: use the workspace (split over d_model) path; False: the single-kernel path."""
@@ -95,6 +96,7 @@ class GpuCase:
 
     def decode(self, num_splits=None):
         from mla_rank_latent_amd import mla
+        assert self.ws is not None, "no decode workspace for this query group"
         mla.mla_decode(self.d, self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.pool, self.block_table,
                        self.seq_lens, self.x["scale"], self.ws, self.out, lse=self.lse, status=self.status,
                        num_splits=self.num_splits if num_splits is None else num_splits)

@@ -155,6 +155,9 @@ def test_append_and_qproj_argument_errors():
     need = lib.mla_cache_append_workspace_bytes(ctypes.byref(v2), 2, 1)
     assert need == 16 * 2 * 576 * 4                     # sixteen K slices of fp32 partial rows
     assert lib.mla_cache_append_workspace_bytes(ctypes.byref(v2), 0, 1) == 0
+    # from 2048 rows the single-GEMM path runs and needs no workspace
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(v2), 1, 2047) == 16 * 2047 * 576 * 4
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(v2), 2, 1024) == 0
     assert lib.mla_cache_append_workspace_bytes(ctypes.byref(mla.dims(8, 16, 8, 32, 64, dtype="f32")), 2, 1) == 0
     ws_small = list(args)
     ws_small[10], ws_small[11] = FAKE, need - 1

@@ -205,3 +205,70 @@ def test_append_paths_agree():
     # rotary part: a rotation can cancel, so one ulp of the rotated pair's length (plus rounding of each side)
     pair = np.sqrt(a[:, 512::2] ** 2 + a[:, 513::2] ** 2).repeat(2, axis=1)
     assert np.all(np.abs(a[:, 512:] - b[:, 512:]) <= 2.0 ** -6 * pair + 1e-30)
+
+
+def _many_token_append_case(seed, dyadic):
+    """2 sequences x 1100 appended tokens = 2200 rows: the single-GEMM append path
+    (2048 rows or more), with a ragged last 128-token tile."""
+    spec = synth.Spec("append_many", batch=2, sq=1100, seq_lens=[1100, 1300], paged=True, append=True, seed=seed,
+                      n_heads=8)
+    x = synth.make_inputs(spec)
+    if dyadic:
+        rng = np.random.default_rng(seed + 1)
+        x["h"] = synth.f32_to_bf16_bits(rng.integers(-2, 3, size=x["h"].shape).astype(np.float32))
+        x["w_dkv"] = synth.f32_to_bf16_bits((rng.integers(-64, 65, size=x["w_dkv"].shape) / 64.0).astype(np.float32))
+        x["w_kr"] = synth.f32_to_bf16_bits((rng.integers(-64, 65, size=x["w_kr"].shape) / 64.0).astype(np.float32))
+    return x
+
+
+def _append_many(x):
+    import torch
+    H.log(f"append_many rows={x['h'].shape[0] * x['h'].shape[1]}")
+    c = H.GpuCase(x)
+    c.append(True)   # the workspace query returns 0 here: the GEMM path needs none
+    torch.cuda.synchronize()
+    return c, c.pool.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_append_many_tokens_dyadic_is_bit_exact():
+    x = _many_token_append_case(31, dyadic=True)
+    before = x["pool"].copy()
+    c, after = _append_many(x)
+    assert int(c.status.item()) == 0
+    rows = H.oracle_append_rows(x)
+    touched = np.zeros(after.shape[:2], dtype=bool)
+    for b in range(2):
+        for t, p in enumerate(x["positions"][b]):
+            blk = x["block_table"][b, p // 64]
+            touched[blk, p % 64] = True
+            want = synth.f32_to_bf16_bits(rows[b, t].astype(np.float32))
+            assert np.array_equal(after[blk, p % 64, :512], want[:512]), (b, t)
+            kr = synth.bf16_bits_to_f32(after[blk, p % 64, 512:]).astype(np.float64)
+            assert np.all(np.abs(kr - rows[b, t, 512:]) <= H.bf16_ulp(rows[b, t, 512:]) + 1e-30), (b, t)
+    assert np.array_equal(after[~touched], before[~touched])
+
+
+def test_append_many_tokens_within_one_ulp():
+    x = _many_token_append_case(33, dyadic=False)
+    c, after = _append_many(x)
+    assert int(c.status.item()) == 0
+    rows = H.oracle_append_rows(x)
+    got = np.stack([[synth.bf16_bits_to_f32(after[x["block_table"][b, p // 64], p % 64]).astype(np.float64)
+                     for p in x["positions"][b]] for b in range(2)])
+    want = rows.astype(np.float64)
+    d = np.abs(got[..., :512] - want[..., :512])
+    rms = np.sqrt(np.mean(want[..., :512] ** 2, axis=-1, keepdims=True))
+    assert np.all(d <= 2.0 ** -7 * np.abs(want[..., :512]) + 2.0 ** -18 * rms)
+    pair = np.sqrt(want[..., 512::2] ** 2 + want[..., 513::2] ** 2).repeat(2, axis=-1)
+    assert np.all(np.abs(got[..., 512:] - want[..., 512:]) <= 2.0 ** -6 * pair + 1e-30)
+
+
+def test_append_many_tokens_bad_position_is_skipped():
+    x = _many_token_append_case(35, dyadic=False)
+    x["positions"] = x["positions"].copy()
+    x["positions"][1, 5] = x["block_table"].shape[1] * 64          # one past the table row
+    before = x["pool"].copy()
+    c, after = _append_many(x)
+    assert int(c.status.item()) & 0x4
+    changed = np.any(after != before, axis=-1)
+    assert changed.sum() == 2200 - 1
