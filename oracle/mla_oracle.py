@@ -43,6 +43,7 @@ import numpy as np
 
 __all__ = [
     "round_to_storage", "rope", "cache_rows", "write_rows", "q_project", "gather_rows",
+    "q_compress", "layer_queries", "out_project",
     "decode", "decode_absorbed", "latent_elements_per_token", "mha_elements_per_token",
     "mqa_elements_per_token", "gqa_elements_per_token",
 ]
@@ -137,6 +138,30 @@ def q_project(h, w_q, w_qr, positions, n_heads: int, rope_base: float):
     qn = (h @ np.asarray(w_q, dtype=np.float64).T).reshape(B, S, n_heads, -1)
     qr = (h @ np.asarray(w_qr, dtype=np.float64).T).reshape(B, S, n_heads, -1)
     return qn, rope(qr, np.asarray(positions)[..., None], rope_base)
+
+
+# ---------------------------------------------------------------------------
+# the full layer's query compression and output projection
+# ([V2] §2.3 and [QD] 02 (3): the query is compressed to c^Q = W^DQ h; [QD]
+# 02 (5): up-projections of c^Q give each head's q^C and its rotary q^R, and
+# the heads' outputs, concatenated, pass through one linear map W^O)
+# ---------------------------------------------------------------------------
+def q_compress(h, w_dq):
+    """c^Q = W^DQ h.  ``h`` [B, S, d], ``w_dq`` [d'_c, d]; returns float64 [B, S, d'_c]."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(w_dq, dtype=np.float64).T
+
+
+def layer_queries(h, w_dq, w_uq, w_qr, positions, n_heads: int, rope_base: float):
+    """q^C_i = W^UQ_i c^Q and q^R_i = RoPE_pos(W^QR_i c^Q) with c^Q = W^DQ h: the
+    query projection of q_project applied to the compressed query."""
+    return q_project(q_compress(h, w_dq), w_uq, w_qr, positions, n_heads, rope_base)
+
+
+def out_project(o, w_o):
+    """u = W^O [o_1; ...; o_{n_h}].  ``o`` [B, S, H, d_h], ``w_o`` [d, H*d_h]; returns [B, S, d]."""
+    o = np.asarray(o, dtype=np.float64)
+    B, S = o.shape[:2]
+    return o.reshape(B, S, -1) @ np.asarray(w_o, dtype=np.float64).T
 
 
 # ---------------------------------------------------------------------------

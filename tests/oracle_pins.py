@@ -392,3 +392,71 @@ def pin_prefill_causal_mha(orc) -> float:
 
 
 ALL_PINS.append(pin_prefill_causal_mha)
+
+
+def _mha_layer_loops(x, wq, wk, wv, wo, H, D):
+    """Textbook MHA layer output at the last position, as loops: per head
+    softmax(q k^T / sqrt(D)) v, heads concatenated, then u = W_O [o_1; ...]."""
+    o = _mha_loops(x, wq, wk, wv, H, D).reshape(-1)
+    d = wo.shape[0]
+    return np.array([sum(wo[r][c] * o[c] for c in range(H * D)) for r in range(d)])
+
+
+def pin_layer_mha_special_case(orc) -> float:
+    """The full layer (query compression, up-projections, attention, output
+    projection) in the MHA special case: W^DQ a random invertible d x d map,
+    W^UQ = W_Q (W^DQ)^-1 so that q^C = W_Q h, no rotary part, W^DKV = [W_K; W_V],
+    W^UK = [I 0], W^UV = [0 I], and W^O = W_O: u must equal the textbook MHA
+    layer output written as loops."""
+    rng = _rng(14)
+    H, D, d, L, dr, bs = 2, 3, 6, 5, 2, 4
+    x = rng.standard_normal((L, d))
+    wq, wk, wv = (rng.standard_normal((H * D, d)) for _ in range(3))
+    wo = rng.standard_normal((d, H * D))
+    w_dq = rng.standard_normal((d, d)) + 3.0 * np.eye(d)
+    w_uq = wq @ np.linalg.inv(w_dq)
+    w_qr = np.zeros((H * dr, d))
+    dc = 2 * H * D
+    w_dkv = np.concatenate([wk, wv], axis=0)
+    eye = np.eye(H * D)
+    w_uk = np.concatenate([eye, np.zeros((H * D, H * D))], axis=1)
+    w_uv = np.concatenate([np.zeros((H * D, H * D)), eye], axis=1)
+    pos = np.arange(L)[None, :]
+    rows = orc.cache_rows(x[None], w_dkv, np.zeros((dr, d)), pos, 10000.0, "f64")
+    nblk = (L + bs - 1) // bs
+    pool = np.full((nblk, bs, dc + dr), 7.0)
+    bt = np.arange(nblk)[None, :]
+    orc.write_rows(pool, bt, pos, rows, bs)
+    qn, qr = orc.layer_queries(x[None, L - 1:L], w_dq, w_uq, w_qr, pos[:, L - 1:], H, 10000.0)
+    out, _ = orc.decode(qn, qr, w_uk, w_uv, pool, bt, [L], 1.0 / math.sqrt(D), bs)
+    u = orc.out_project(out, wo)
+    ref = _mha_layer_loops(x, wq, wk, wv, wo, H, D)
+    return float(np.max(np.abs(u[0, 0] - ref)))
+
+
+def pin_layer_queries_rotary(orc) -> float:
+    """The compressed query's rotary part: with one head, W^DQ = I (a d-wide
+    query latent) and W^QR = W^KR, q^R . k^R at the same position equals
+    |W^KR h|^2 (both sides turned by the same rotation); and q^C equals
+    W^UQ (W^DQ h) summed by hand."""
+    rng = _rng(15)
+    d, dr, dc = 8, 4, 3
+    w_kr = rng.standard_normal((dr, d))
+    w_dkv = rng.standard_normal((dc, d))
+    w_dq = np.eye(d)
+    w_uq = rng.standard_normal((5, d))
+    err = 0.0
+    for p in [0, 3, 4096]:
+        h = rng.standard_normal((1, 1, d))
+        pos = np.array([[p]])
+        row = orc.cache_rows(h, w_dkv, w_kr, pos, 10000.0, "f64")
+        qn, qr = orc.layer_queries(h, w_dq, w_uq, w_kr, pos, 1, 10000.0)
+        want = float(np.sum((w_kr @ h[0, 0]) ** 2))
+        err = max(err, abs(float(qr[0, 0, 0] @ row[0, 0, dc:]) - want) / want)
+        hand = [sum(w_uq[r][c] * h[0, 0, c] for c in range(d)) for r in range(5)]
+        err = max(err, float(np.max(np.abs(qn[0, 0, 0] - hand))))
+    return err
+
+
+ALL_PINS.append(pin_layer_mha_special_case)
+ALL_PINS.append(pin_layer_queries_rotary)

@@ -57,6 +57,10 @@ MUTANTS = {
                           "                n = L - Sq + s + (s == 0)\n                if n <= 0:\n                    out[b, s, i], lse[b, s, i] = 0.0, -np.inf\n                    continue\n                q = np.concatenate"),
     "causal_group_sees_all": ("                n = L - Sq + s + 1\n                if n <= 0:",
                               "                n = L\n                if n <= 0:"),
+    "out_project_transposed": ("return o.reshape(B, S, -1) @ np.asarray(w_o, dtype=np.float64).T",
+                               "return o.reshape(B, S, -1) @ np.asarray(w_o, dtype=np.float64)"),
+    "layer_queries_uncompressed": ("return q_project(q_compress(h, w_dq), w_uq, w_qr, positions, n_heads, rope_base)",
+                                   "return q_project(h, w_uq, w_qr, positions, n_heads, rope_base)"),
     "scale_dropped": ("_softmax_attend(scale * (k[:n] @ q), v[:n])", "_softmax_attend((k[:n] @ q), v[:n])"),
     "softmax_unnormalised": ("return (e / den) @ v, m + math.log(den)", "return (e / len(e)) @ v, m + math.log(den)"),
     "bf16_nine_bits": ("return _round_significand(x, 8, -126, 127)", "return _round_significand(x, 9, -126, 127)"),
