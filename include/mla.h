@@ -230,6 +230,41 @@ int mla_decode_finish(const mla_dims* dims, const void* q_nope, const void* q_ro
                       int32_t* status, void* stream);
 
 /*
+ * The full layer's projections around attention ("DeepSeek-V2 ... MLA" page
+ * §2.3 query compression; "【深度学习】DeepSeek焦点架构-MLA" page 02 (3) and
+ * (5): the compressed query's up-projections give each head's q^C and its
+ * rotary q^R, and the heads' outputs, concatenated, pass through W^O).
+ * bf16 only (f32: MLA_ERR_UNSUPPORTED); d_model and d_qlat multiples of 64;
+ * batch * sq <= 2^20.  Products accumulate in fp32, split over the input
+ * features across workgroups and summed in a fixed order, so results do not
+ * depend on timing.
+ *
+ * Workspace bytes for mla_q_compress and mla_out_project with this shape
+ * (the larger of the two); 0 for invalid or unsupported arguments.
+ */
+size_t mla_layer_workspace_bytes(const mla_dims* dims, int32_t d_qlat, int32_t batch, int32_t sq);
+
+/*
+ *   c^Q          = W^DQ h              (w_dq [d_qlat, d_model]); kept in bf16
+ *   q_nope[.., i] = W^UQ_i c^Q         (w_uq [n_heads*d_nope, d_qlat])
+ *   q_rope[.., i] = RoPE_p(W^QR_i c^Q) (w_qr [n_heads*d_rope, d_qlat]), p = positions[b*sq + s]
+ * h [batch, sq, d_model]; positions [batch, sq] int32 (device); q_nope and
+ * q_rope as mla_decode takes them.  RoPE as in mla_cache_append.
+ */
+int mla_q_compress(const mla_dims* dims, int32_t d_qlat, const void* h, const void* w_dq,
+                   const void* w_uq, const void* w_qr, const int32_t* positions,
+                   void* q_nope, void* q_rope, int32_t batch, int32_t sq,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ *   u[b, s, :] = W^O [o_1; ...; o_{n_heads}]   (w_o [d_model, n_heads*d_nope])
+ * o [batch, sq, n_heads, d_nope] (mla_decode's out); u [batch, sq, d_model].
+ */
+int mla_out_project(const mla_dims* dims, const void* o, const void* w_o, void* u,
+                    int32_t batch, int32_t sq, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * Workspace bytes mla_prefill needs: the expanded per-head keys and values of
  * every token slot the block table can address,
  *   2 * batch * n_heads * (max_blocks * block_size) * d_nope * 2 bytes.

@@ -1,6 +1,7 @@
 // Host entry points of the MLA decode library (the C ABI declared in mla.h).
 // Every check that the arguments allow is made here, before anything is
 // launched; the kernels only guard against what the data alone can reveal.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 
@@ -179,6 +180,78 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
   else
     e = launch_append_f32(dims, (const float*)h, (const float*)w_dkv, (const float*)w_kr, positions, block_table,
                           max_blocks, (float*)cache, num_blocks, batch * t, t, status, st);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+namespace {
+// the full layer's projections run on bf16 tiles of 64 features (d_qlat 0: not used by the call)
+int check_layer(const mla_dims* d, int d_qlat, int batch, int sq) {
+  int rc = check_dims(d);
+  if (rc != MLA_OK) return rc;
+  if (d->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (d_qlat != 0 && (d_qlat < 64 || d_qlat % 64 != 0)) return MLA_ERR_UNSUPPORTED;
+  if (d->d_model % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (d_qlat > (1 << 16)) return MLA_ERR_CAPACITY;
+  if (batch < 1 || sq < 1) return MLA_ERR_BAD_DIMS;
+  if ((long long)batch * sq > (1 << 20)) return MLA_ERR_CAPACITY;
+  return MLA_OK;
+}
+size_t q_compress_bytes(const mla_dims* d, int d_qlat, int M) {
+  const size_t cq = up((size_t)M * d_qlat * 2);
+  size_t part = proj_ws_bytes(M, d_qlat, d->d_model);
+  part = std::max(part, proj_ws_bytes(M, d->n_heads * d->d_nope, d_qlat));
+  part = std::max(part, proj_ws_bytes(M, d->n_heads * d->d_rope, d_qlat));
+  return cq + up(part);
+}
+}  // namespace
+
+size_t mla_layer_workspace_bytes(const mla_dims* dims, int32_t d_qlat, int32_t batch, int32_t sq) {
+  if (check_layer(dims, d_qlat, batch, sq) != MLA_OK) return 0;
+  const int M = batch * sq;
+  return std::max(q_compress_bytes(dims, d_qlat, M),
+                  up(proj_ws_bytes(M, dims->d_model, dims->n_heads * dims->d_nope)));
+}
+
+int mla_q_compress(const mla_dims* dims, int32_t d_qlat, const void* h, const void* w_dq, const void* w_uq,
+                   const void* w_qr, const int32_t* positions, void* q_nope, void* q_rope, int32_t batch, int32_t sq,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layer(dims, d_qlat, batch, sq);
+  if (rc != MLA_OK) return rc;
+  if (!h || !w_dq || !w_uq || !w_qr || !positions || !q_nope || !q_rope || !workspace) return MLA_ERR_NULL_PTR;
+  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(w_qr) || !aligned16(positions) ||
+      !aligned16(q_nope) || !aligned16(q_rope) || ((uintptr_t)workspace & (kAlign - 1)))
+    return MLA_ERR_BAD_ALIGN;
+  const int M = batch * sq;
+  if (workspace_bytes < q_compress_bytes(dims, d_qlat, M)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t* cq = (uint16_t*)workspace;
+  float* part = (float*)((uint8_t*)workspace + up((size_t)M * d_qlat * 2));
+  const int HN = dims->n_heads * dims->d_nope, HR = dims->n_heads * dims->d_rope;
+  // c^Q = W^DQ h (kept in bf16, the activation type), then q^C = W^UQ c^Q and q^R = RoPE(W^QR c^Q)
+  hipError_t e = launch_proj_bf16((const uint16_t*)h, (const uint16_t*)w_dq, M, d_qlat, dims->d_model, part, d_qlat,
+                                  dims->d_rope, positions, dims->rope_base, cq, d_qlat, nullptr, 0, st);
+  if (e == hipSuccess)
+    e = launch_proj_bf16(cq, (const uint16_t*)w_uq, M, HN, d_qlat, part, HN, dims->d_rope, positions, dims->rope_base,
+                         (uint16_t*)q_nope, HN, nullptr, 0, st);
+  if (e == hipSuccess)
+    e = launch_proj_bf16(cq, (const uint16_t*)w_qr, M, HR, d_qlat, part, 0, dims->d_rope, positions, dims->rope_base,
+                         nullptr, 0, (uint16_t*)q_rope, HR, st);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_out_project(const mla_dims* dims, const void* o, const void* w_o, void* u, int32_t batch, int32_t sq,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layer(dims, 0, batch, sq);
+  if (rc != MLA_OK) return rc;
+  if (!o || !w_o || !u || !workspace) return MLA_ERR_NULL_PTR;
+  if (!aligned16(o) || !aligned16(w_o) || !aligned16(u) || ((uintptr_t)workspace & (kAlign - 1)))
+    return MLA_ERR_BAD_ALIGN;
+  const int M = batch * sq;
+  const int HN = dims->n_heads * dims->d_nope;
+  if (workspace_bytes < proj_ws_bytes(M, dims->d_model, HN)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_proj_bf16((const uint16_t*)o, (const uint16_t*)w_o, M, dims->d_model, HN, (float*)workspace,
+                                  dims->d_model, dims->d_rope, nullptr, dims->rope_base, (uint16_t*)u, dims->d_model,
+                                  nullptr, 0, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

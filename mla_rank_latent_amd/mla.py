@@ -24,7 +24,7 @@ MLA_STATUS_BAD_POS = 0x4
 EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_append_workspace_bytes",
            "mla_q_project", "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
            "mla_decode_finish", "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_expand",
-           "mla_prefill_attend")
+           "mla_prefill_attend", "mla_layer_workspace_bytes", "mla_q_compress", "mla_out_project")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or python -m mla_rank_latent_amd.build)")
@@ -65,6 +65,13 @@ _lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I, _I]
 _lib.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
 _lib.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I]
+_lib.mla_layer_workspace_bytes.restype = ctypes.c_size_t
+_lib.mla_layer_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I, _I]
+_lib.mla_q_compress.restype = ctypes.c_int
+_lib.mla_q_compress.argtypes = [ctypes.POINTER(MlaDims), _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, ctypes.c_size_t,
+                                _P]
+_lib.mla_out_project.restype = ctypes.c_int
+_lib.mla_out_project.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _I, _I, _P, ctypes.c_size_t, _P]
 for _name in ("mla_prefill", "mla_prefill_expand", "mla_prefill_attend"):
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
@@ -117,6 +124,43 @@ def mla_decode_workspace_bytes(d: MlaDims, batch: int, sq: int, num_splits: int 
 
 def mla_prefill_workspace_bytes(d: MlaDims, batch: int, max_blocks: int) -> int:
     return int(_lib.mla_prefill_workspace_bytes(ctypes.byref(d), batch, max_blocks))
+
+
+def mla_layer_workspace_bytes(d: MlaDims, d_qlat: int, batch: int, sq: int) -> int:
+    return int(_lib.mla_layer_workspace_bytes(ctypes.byref(d), d_qlat, batch, sq))
+
+
+def prepared_q_compress(d: MlaDims, d_qlat: int, h, w_dq, w_uq, w_qr, positions, q_nope, q_rope, workspace,
+                        stream=None):
+    """h [batch, sq, d_model] -> q_nope, q_rope (as mla_decode takes them) through the compressed query;
+    returns a zero-argument launcher (arguments marshalled once, return code checked on every call)."""
+    batch, sq = int(h.shape[0]), int(h.shape[1])
+    args = (ctypes.byref(d), d_qlat, _ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(positions), _ptr(q_nope),
+            _ptr(q_rope), batch, sq, _ptr(workspace), _nbytes(workspace), _stream(stream))
+
+    def launch() -> None:
+        _check("mla_q_compress", _lib.mla_q_compress(*args))
+    return launch
+
+
+def mla_q_compress(d: MlaDims, d_qlat: int, h, w_dq, w_uq, w_qr, positions, q_nope, q_rope, workspace,
+                   stream=None) -> None:
+    prepared_q_compress(d, d_qlat, h, w_dq, w_uq, w_qr, positions, q_nope, q_rope, workspace, stream)()
+
+
+def prepared_out_project(d: MlaDims, o, w_o, u, workspace, stream=None):
+    """o [batch, sq, n_heads, d_nope] -> u [batch, sq, d_model]; returns a zero-argument launcher."""
+    batch, sq = int(o.shape[0]), int(o.shape[1])
+    args = (ctypes.byref(d), _ptr(o), _ptr(w_o), _ptr(u), batch, sq, _ptr(workspace), _nbytes(workspace),
+            _stream(stream))
+
+    def launch() -> None:
+        _check("mla_out_project", _lib.mla_out_project(*args))
+    return launch
+
+
+def mla_out_project(d: MlaDims, o, w_o, u, workspace, stream=None) -> None:
+    prepared_out_project(d, o, w_o, u, workspace, stream)()
 
 
 def mla_cache_append_workspace_bytes(d: MlaDims, batch: int, t: int) -> int:

@@ -24,6 +24,8 @@ Draw order inside one workload is fixed:
   5. W_UK then W_UV
   6. append inputs: h_new, W_DKV, W_KR
   7. query-projection inputs: W_Q, W_QR (their hidden state is the appended h)
+  8. full-layer inputs (layer workloads): W_DQ, W_UQ, W_QR, W_O; the queries'
+     hidden state is the appended h
 Cache rows that hold no token (past a sequence's end, or the slot the append
 will fill) are set to a finite sentinel, so a kernel that reads them by
 mistake produces visibly wrong numbers.
@@ -72,6 +74,8 @@ class Spec:
     paged: bool = True               # False: identity block table (contiguous cache)
     append: bool = False             # append the last sq tokens from hidden states
     q_from_hidden: bool = False      # queries come from projecting the appended hidden states
+    layer: bool = False              # the full layer: compressed queries from h, output projection W^O
+    d_qlat: int = 1536               # d'_c, the query latent width (layer workloads)
     scale: Optional[float] = None    # default 1/sqrt(d_nope + d_rope)
 
     @property
@@ -113,6 +117,14 @@ def _normals(rng: np.random.Generator, n: int, scale: float, dtype: str) -> np.n
 
 def _weight(rng, out_f: int, in_f: int, dtype: str) -> np.ndarray:
     return _normals(rng, out_f * in_f, 1.0 / math.sqrt(in_f), dtype).reshape(out_f, in_f)
+
+
+def layer_presets() -> Dict[str, Spec]:
+    """Full-layer decode workloads: the batch-64 context-8192 step with query compression and W^O."""
+    return {
+        "layer_b64_ctx8192": Spec("layer_b64_ctx8192", batch=64, sq=1, seed=7, seq_lens=[8192] * 64, paged=True,
+                                  append=True, layer=True),
+    }
 
 
 def prefill_presets() -> Dict[str, Spec]:
@@ -177,6 +189,15 @@ def make_inputs(spec: Spec) -> Dict[str, object]:
         out["w_q"] = _weight(rng, H * dn, d, spec.dtype)
         out["w_qr"] = _weight(rng, H * dr, d, spec.dtype)
         # the last sq appended tokens are the queries
+        out["q_positions"] = out["positions"][:, -spec.sq:].copy()
+    if spec.layer:
+        if not spec.append:
+            raise ValueError("layer workloads append the query tokens' hidden states")
+        dq = spec.d_qlat
+        out["w_dq"] = _weight(rng, dq, d, spec.dtype)
+        out["w_uq"] = _weight(rng, H * dn, dq, spec.dtype)
+        out["w_qr_c"] = _weight(rng, H * dr, dq, spec.dtype)
+        out["w_o"] = _weight(rng, d, H * dn, spec.dtype)
         out["q_positions"] = out["positions"][:, -spec.sq:].copy()
     return out
 

@@ -110,6 +110,34 @@ class GpuCase:
         self.decode()
 
 
+class LayerCase(GpuCase):
+    """A GpuCase whose queries come from the full layer's compressed query path
+    and whose output goes through W^O."""
+
+    def __init__(self, x: dict, num_splits: int = 0):
+        import torch
+        from mla_rank_latent_amd import mla
+        super().__init__(x, num_splits)
+        spec = self.spec
+        B, S = spec.batch, spec.sq
+        self.w_dq, self.w_uq = dev(x["w_dq"], spec.dtype), dev(x["w_uq"], spec.dtype)
+        self.w_qr_c, self.w_o = dev(x["w_qr_c"], spec.dtype), dev(x["w_o"], spec.dtype)
+        self.q_positions = dev(x["q_positions"], spec.dtype)
+        self.h_q = self.h[:, -S:].contiguous()
+        self.u = torch.empty(B, S, spec.d_model, dtype=torch.bfloat16, device="cuda")
+        n = mla.mla_layer_workspace_bytes(self.d, spec.d_qlat, B, S)
+        assert n > 0
+        self.lws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def layer_step(self):
+        from mla_rank_latent_amd import mla
+        self.append(self.split_append)
+        mla.mla_q_compress(self.d, self.spec.d_qlat, self.h_q, self.w_dq, self.w_uq, self.w_qr_c, self.q_positions,
+                           self.q_nope, self.q_rope, self.lws)
+        self.decode()
+        mla.mla_out_project(self.d, self.out, self.w_o, self.u, self.lws)
+
+
 class PrefillCase:
     """Device copies of a generated workload whose sq query tokens are a prefill chunk."""
 
@@ -192,6 +220,20 @@ def oracle_query_samples(x: dict, samples):
                                  [n], x["scale"], bs, heads=[h])
         res.append((o[0, 0, h], l[0, 0, h]))
     return res
+
+
+def oracle_layer(x: dict, batches=None):
+    """Oracle u [B, S, d] (rows not in ``batches`` NaN) for a layer workload: the
+    appended rows as the cache stores them, the compressed-query path, decode and
+    W^O, in fp64 with no other rounding."""
+    spec = x["spec"]
+    f = lambda k: synth.as_float(x[k], spec.dtype)
+    rows = oracle_append_rows(x)
+    h_q = f("h")[:, -spec.sq:]
+    qn, qr = mla_oracle.layer_queries(h_q, f("w_dq"), f("w_uq"), f("w_qr_c"), x["q_positions"], spec.n_heads,
+                                      spec.rope_base)
+    out, _ = oracle_decode(x, batches=batches, appended_rows=rows, q=(qn, qr))
+    return mla_oracle.out_project(np.nan_to_num(out, nan=0.0), f("w_o")), qn, qr
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:
