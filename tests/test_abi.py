@@ -140,6 +140,41 @@ def test_prefill_workspace_and_argument_errors():
         assert _prefill(mla.dims(128, 128, 64, 512, 5120, block_size=32), fn) == -8
 
 
+def test_layer_workspace_and_argument_errors():
+    lib = mla.raw_library()
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    n = mla.mla_layer_workspace_bytes(v2, 1536, 64, 1)
+    # at least the bf16 compressed query plus one fp32 copy of each projection's output
+    assert n >= 64 * 1536 * 2 + 64 * 128 * 128 * 4
+    assert n >= 64 * 5120 * 4
+    assert mla.mla_layer_workspace_bytes(v2, 1000, 64, 1) == 0                 # d_qlat not a multiple of 64
+    assert mla.mla_layer_workspace_bytes(mla.dims(128, 128, 64, 512, 5120 - 32), 1536, 64, 1) == 0
+    assert mla.mla_layer_workspace_bytes(mla.dims(8, 16, 8, 32, 64, dtype="f32"), 1536, 1, 1) == 0
+    assert mla.mla_layer_workspace_bytes(v2, 1536, 0, 1) == 0
+    qc = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1, FAKE, n, None]
+    bad = list(qc)
+    bad[0] = None
+    assert lib.mla_q_compress(ctypes.byref(v2), 1536, *bad) == -1
+    bad = list(qc)
+    bad[10] = 1024           # far below what the call needs (every call here must fail before any launch)
+    assert lib.mla_q_compress(ctypes.byref(v2), 1536, *bad) == -5
+    bad = list(qc)
+    bad[3] = FAKE + 2
+    assert lib.mla_q_compress(ctypes.byref(v2), 1536, *bad) == -4
+    assert lib.mla_q_compress(ctypes.byref(v2), 96, *qc) == -8
+    assert lib.mla_q_compress(ctypes.byref(mla.dims(8, 16, 8, 32, 64, dtype="f32")), 1536, *qc) == -8
+    op = [FAKE, FAKE, FAKE, 64, 1, FAKE, n, None]
+    bad = list(op)
+    bad[2] = None
+    assert lib.mla_out_project(ctypes.byref(v2), *bad) == -1
+    bad = list(op)
+    bad[4] = 0
+    assert lib.mla_out_project(ctypes.byref(v2), *bad) == -2
+    bad = list(op)
+    bad[6] = 1024
+    assert lib.mla_out_project(ctypes.byref(v2), *bad) == -5
+
+
 def test_append_and_qproj_argument_errors():
     lib = mla.raw_library()
     v2 = mla.dims(128, 128, 64, 512, 5120)
