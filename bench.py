@@ -233,6 +233,171 @@ def run_prefill(args, spec, x) -> int:
     return 0
 
 
+def layer_extra(spec):
+    """Bytes and flops the full layer adds to a decode step: W^DQ, W^UQ, W^QR and W^O,
+    and the output u (the hidden states are already counted by the append)."""
+    H, dn, dr, d, dq = spec.n_heads, spec.d_nope, spec.d_rope, spec.d_model, spec.d_qlat
+    M = spec.batch * spec.sq
+    w = (dq * d + H * (dn + dr) * dq + d * H * dn) * 2
+    flops = 2 * M * (dq * d + H * (dn + dr) * dq + d * H * dn)
+    return dict(bytes=w + M * d * 2, flops=flops)
+
+
+def run_layer(args, spec, x) -> int:
+    """Full-layer decode step: append, compressed queries, decode (three phases), W^O."""
+    import torch
+    from mla_rank_latent_amd import mla
+
+    def dev(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, spec.dtype,
+                 spec.rope_base)
+    B, S = spec.batch, spec.sq
+    pool, bt, lens = dev(x["pool"]), dev(x["block_table"]), dev(x["seq_lens"])
+    w_uk, w_uv = dev(x["w_uk"]), dev(x["w_uv"])
+    h, w_dkv, w_kr, pos = dev(x["h"]), dev(x["w_dkv"]), dev(x["w_kr"]), dev(x["positions"])
+    w_dq, w_uq, w_qr, w_o = dev(x["w_dq"]), dev(x["w_uq"]), dev(x["w_qr_c"]), dev(x["w_o"])
+    q_pos = dev(x["q_positions"])
+    h_q = h[:, -S:].contiguous()
+    qn = torch.empty(B, S, spec.n_heads, spec.d_nope, dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty(B, S, spec.n_heads, spec.d_rope, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(B, S, spec.n_heads, spec.d_nope, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, S, spec.n_heads, dtype=torch.float32, device="cuda")
+    u = torch.empty(B, S, spec.d_model, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_bytes(d, B, S, args.num_splits), dtype=torch.uint8, device="cuda")
+    lws = torch.empty(mla.mla_layer_workspace_bytes(d, spec.d_qlat, B, S), dtype=torch.uint8, device="cuda")
+    n_ws = mla.mla_cache_append_workspace_bytes(d, int(h.shape[0]), int(h.shape[1]))
+    append_ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws else None
+    stream = torch.cuda.current_stream()
+    append = mla.prepared_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, workspace=append_ws, stream=stream)
+    qcomp = mla.prepared_q_compress(d, spec.d_qlat, h_q, w_dq, w_uq, w_qr, q_pos, qn, qr, lws, stream=stream)
+    dec_args = (d, qn, qr, w_uk, w_uv, pool, bt, lens, x["scale"], ws, out)
+    phase = {name: mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
+             for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish")}
+    oproj = mla.prepared_out_project(d, out, w_o, u, lws, stream=stream)
+
+    def step(ev_a=None, ev_b=None):
+        append()
+        qcomp()
+        phase["mla_decode_prepare"]()
+        if ev_a is not None:
+            ev_a.record(stream)
+        phase["mla_decode_attend"]()
+        if ev_b is not None:
+            ev_b.record(stream)
+        phase["mla_decode_finish"]()
+        oproj()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(ev_a[i], ev_b[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_attn = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
+          f"attention {ms_attn * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    wl = workload_bytes_flops(spec, x["seq_lens"])
+    ex = layer_extra(spec)
+    # decode's bytes (cache, W^UK/W^UV, queries, o) plus the layer's weights and its output u
+    step_bytes = wl["bytes"] + ex["bytes"]
+    step_flops = wl["flops"] + ex["flops"]
+    step_s = ms_step * 1e-3
+    gbs = step_bytes / step_s / 1e9
+    attn_gbs = wl["cache_bytes"] / (ms_attn * 1e-3) / 1e9
+    attn_tflops = wl["attn_flops"] / (ms_attn * 1e-3) / 1e12
+    res = {
+        "metric": "MLA full-layer decode GB/s (% roofline), tokens/s; B=64 ctx=8K 128 heads, d'_c=1536",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) cache/hidden states, N(0,1/fan_in) weights)",
+        "config": {"workload": spec.name, "batch": B, "context": int(max(x["seq_lens"])), "query_tokens": S,
+                   "heads": spec.n_heads, "d_latent": spec.d_latent, "d_rope": spec.d_rope, "d_nope": spec.d_nope,
+                   "d_model": spec.d_model, "d_qlat": spec.d_qlat, "block_size": spec.block_size,
+                   "paged": spec.paged, "append": spec.append, "num_splits": args.num_splits or "auto"},
+        "tflops": round(step_flops / step_s / 1e12, 2),
+        "tokens_per_s": round(B * S / step_s, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "step_bytes": step_bytes,
+        "step_flops": step_flops,
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(spec.name),
+                     "kernel": "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
+                     "bytes_per_launch": wl["cache_bytes"], "mfma_tflops": round(attn_tflops, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (oracle, ~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_layer(x, args.cpu_budget, step_bytes)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline_layer(x, budget_s: float, step_bytes: int):
+    """The fp64 oracle on whole sequences of the layer workload (appended row, compressed
+    queries, decode over all heads, W^O) until ``budget_s`` is spent; GB/s of the step's bytes
+    in proportion to the sequences done."""
+    import numpy as np
+    from mla_rank_latent_amd import synth
+    from oracle import mla_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = x["spec"]
+    bs = spec.block_size
+    f = lambda k: synth.as_float(x[k], spec.dtype)
+    w_uk, w_uv, w_dq, w_uq, w_qr, w_o = f("w_uk"), f("w_uv"), f("w_dq"), f("w_uq"), f("w_qr_c"), f("w_o")
+    w_dkv, w_kr = f("w_dkv"), f("w_kr")
+    done, spent = 0, 0.0
+    for b in range(spec.batch):
+        L = int(x["seq_lens"][b])
+        nblk = (L + bs - 1) // bs
+        sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)
+        t0 = time.perf_counter()
+        hb = synth.as_float(x["h"][b:b + 1], spec.dtype)
+        rows = mla_oracle.cache_rows(hb, w_dkv, w_kr, x["positions"][b:b + 1], spec.rope_base, spec.dtype)
+        for t, p in enumerate(x["positions"][b]):
+            sub[p // bs, p % bs] = rows[0, t]
+        qn, qr = mla_oracle.layer_queries(hb[:, -spec.sq:], w_dq, w_uq, w_qr, x["q_positions"][b:b + 1],
+                                          spec.n_heads, spec.rope_base)
+        o, _ = mla_oracle.decode(qn, qr, w_uk, w_uv, sub, np.arange(nblk)[None, :], [L], x["scale"], bs)
+        mla_oracle.out_project(o, w_o)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    value = step_bytes * done / spec.batch / spent / 1e9
+    return {"value": round(value, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {spec.batch} sequences (append, compressed queries, all {spec.n_heads} heads, "
+                      f"W^O) in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
+
+
 def cpu_baseline(x, budget_s: float):
     """Time the fp64 oracle (as it stands) on whole sequences of the workload until
     ``budget_s`` of CPU work has been spent; scale to GB/s of the same algorithmic bytes."""
@@ -304,12 +469,14 @@ def main() -> int:
         print(json.dumps({"copy_bytes_per_dispatch": 1 << 30, "dispatches": 3}), flush=True)
         return 0
 
-    prefill = synth.prefill_presets()
-    spec = prefill[args.workload] if args.workload in prefill else synth.presets()[args.workload]
+    prefill, layer = synth.prefill_presets(), synth.layer_presets()
+    spec = {**synth.presets(), **prefill, **layer}[args.workload]
     print(f"[bench] generating {spec.name} (seed {spec.seed})", file=sys.stderr, flush=True)
     x = synth.make_inputs(spec)
     if args.workload in prefill:
         return run_prefill(args, spec, x)
+    if args.workload in layer:
+        return run_layer(args, spec, x)
 
     def dev(a):
         import numpy as np

@@ -199,8 +199,7 @@ int check_layer(const mla_dims* d, int d_qlat, int batch, int sq) {
 size_t q_compress_bytes(const mla_dims* d, int d_qlat, int M) {
   const size_t cq = up((size_t)M * d_qlat * 2);
   size_t part = proj_ws_bytes(M, d_qlat, d->d_model);
-  part = std::max(part, proj_ws_bytes(M, d->n_heads * d->d_nope, d_qlat));
-  part = std::max(part, proj_ws_bytes(M, d->n_heads * d->d_rope, d_qlat));
+  part = std::max(part, proj_ws_bytes(M, d->n_heads * (d->d_nope + d->d_rope), d_qlat));
   return cq + up(part);
 }
 }  // namespace
@@ -227,15 +226,14 @@ int mla_q_compress(const mla_dims* dims, int32_t d_qlat, const void* h, const vo
   uint16_t* cq = (uint16_t*)workspace;
   float* part = (float*)((uint8_t*)workspace + up((size_t)M * d_qlat * 2));
   const int HN = dims->n_heads * dims->d_nope, HR = dims->n_heads * dims->d_rope;
-  // c^Q = W^DQ h (kept in bf16, the activation type), then q^C = W^UQ c^Q and q^R = RoPE(W^QR c^Q)
-  hipError_t e = launch_proj_bf16((const uint16_t*)h, (const uint16_t*)w_dq, M, d_qlat, dims->d_model, part, d_qlat,
+  // c^Q = W^DQ h (kept in bf16, the activation type), then q^C = W^UQ c^Q and q^R = RoPE(W^QR c^Q) as one
+  // product over the stacked rows [W^UQ; W^QR]
+  const uint16_t* wdq = (const uint16_t*)w_dq;
+  hipError_t e = launch_proj_bf16((const uint16_t*)h, wdq, wdq, d_qlat, M, d_qlat, dims->d_model, part, d_qlat,
                                   dims->d_rope, positions, dims->rope_base, cq, d_qlat, nullptr, 0, st);
   if (e == hipSuccess)
-    e = launch_proj_bf16(cq, (const uint16_t*)w_uq, M, HN, d_qlat, part, HN, dims->d_rope, positions, dims->rope_base,
-                         (uint16_t*)q_nope, HN, nullptr, 0, st);
-  if (e == hipSuccess)
-    e = launch_proj_bf16(cq, (const uint16_t*)w_qr, M, HR, d_qlat, part, 0, dims->d_rope, positions, dims->rope_base,
-                         nullptr, 0, (uint16_t*)q_rope, HR, st);
+    e = launch_proj_bf16(cq, (const uint16_t*)w_uq, (const uint16_t*)w_qr, HN, M, HN + HR, d_qlat, part, HN,
+                         dims->d_rope, positions, dims->rope_base, (uint16_t*)q_nope, HN, (uint16_t*)q_rope, HR, st);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -248,8 +246,9 @@ int mla_out_project(const mla_dims* dims, const void* o, const void* w_o, void* 
     return MLA_ERR_BAD_ALIGN;
   const int M = batch * sq;
   const int HN = dims->n_heads * dims->d_nope;
-  if (workspace_bytes < proj_ws_bytes(M, dims->d_model, HN)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  hipError_t e = launch_proj_bf16((const uint16_t*)o, (const uint16_t*)w_o, M, dims->d_model, HN, (float*)workspace,
+  if (workspace_bytes < std::max<size_t>(proj_ws_bytes(M, dims->d_model, HN), 1)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const uint16_t* wo = (const uint16_t*)w_o;
+  hipError_t e = launch_proj_bf16((const uint16_t*)o, wo, wo, dims->d_model, M, dims->d_model, HN, (float*)workspace,
                                   dims->d_model, dims->d_rope, nullptr, dims->rope_base, (uint16_t*)u, dims->d_model,
                                   nullptr, 0, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

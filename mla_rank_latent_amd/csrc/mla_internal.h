@@ -95,9 +95,9 @@ hipError_t launch_append_gemm_bf16(const uint16_t* h, const uint16_t* w_dkv, con
 // full-layer projections: y = x W^T for a few rows, split over K, summed in order
 int proj_splits(int M, int N, int K);
 size_t proj_ws_bytes(int M, int N, int K);
-hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, int M, int N, int K, float* part, int rope_from,
-                            int rope_width, const int32_t* positions, float rope_base, uint16_t* y0, int ld0,
-                            uint16_t* y1, int ld1, hipStream_t st);
+hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int n_w0, int M, int N, int K,
+                            float* part, int rope_from, int rope_width, const int32_t* positions, float rope_base,
+                            uint16_t* y0, int ld0, uint16_t* y1, int ld1, hipStream_t st);
 // prefill (expanded form): workspace bytes, K^C / V^T expansion, causal attention
 size_t prefill_ws_bytes(int batch, int n_heads, int max_blocks);
 hipError_t launch_expand_kv_bf16(const uint16_t* cache, int num_blocks, const int32_t* block_table, int max_blocks,

@@ -7,16 +7,18 @@
 //   u   = W^O [o_1; ...; o_{n_h}]        (same, 02 (5): the heads' outputs, concatenated,
 //                                          through one linear map)
 // With so few rows the weights dominate the bytes: the kernel streams them once.
+// W may be two stacked matrices (q^C and q^R come from [W^UQ; W^QR] in one pass).
 // proj_partial_bf16_kernel: workgroup (64-row tile, 64-column tile, K split);
 //   the x rows and W rows of the split stream through a 3-slot LDS ring in
 //   64-feature chunks (direct-to-LDS copies of 1 KB, 16-byte chunk c of a
 //   128-byte LDS row r at c ^ ((r >> 1) & 7)); wave (mh, nh) accumulates rows
-//   32 mh .. +31 x columns 32 nh .. +31 on MFMA 32x32x16 and stores its fp32
-//   partial.
+//   32 mh .. +31 x columns 32 nh .. +31 on MFMA 32x32x16.  Split over K, it
+//   stores its fp32 partial; unsplit (enough column tiles to fill the chip),
+//   it writes bf16 itself, taking a rotary pair's partner from the next lane.
 // proj_finish_bf16_kernel: sums the splits of each element in split order (so
-//   the result does not depend on timing) and writes bf16; columns at or past
-//   `rope_from` are the rotary query, whose pairs (2j, 2j + 1) within each
-//   64-wide head turn by angle pos * base^(-2j/64) in fp64 before rounding.
+//   the result does not depend on timing) and writes bf16.
+// Columns at or past `rope_from` are the rotary query: pairs (2j, 2j + 1) of
+// each 64-wide head turn by angle pos * base^(-2j/64) in fp64 before rounding.
 #include "device_util.h"
 
 namespace mla {
@@ -35,10 +37,21 @@ __device__ __forceinline__ void dma16_at(uint64_t addr, uint32_t lds_addr) {
 __device__ __forceinline__ int pswz(int r) { return (r >> 1) & 7; }
 }  // namespace
 
+struct ProjOut {               // direct bf16 output (one split): columns < rope_from -> y0, the rest -> y1
+  uint16_t* y0;
+  int ld0;
+  uint16_t* y1;
+  int ld1;
+  int rope_from, rope_width;
+  const int32_t* positions;
+  double rope_base;
+};
+
 __global__ __launch_bounds__(256) void proj_partial_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ w, int M, int N, int K,
-                                                                int splits, int chunks_per_split,
-                                                                float* __restrict__ part) {
+                                                                const uint16_t* __restrict__ w0,
+                                                                const uint16_t* __restrict__ w1, int n_w0, int M,
+                                                                int N, int K, int splits, int chunks_per_split,
+                                                                float* __restrict__ part, ProjOut po) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPStages * kPChunk];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
   const int n_tiles = N / kPT;
@@ -63,7 +76,9 @@ __global__ __launch_bounds__(256) void proj_partial_bf16_kernel(const uint16_t* 
       const int m = m0 + r < M ? m0 + r : M - 1;
       rowp = x + (size_t)m * K;
     } else {
-      rowp = w + (size_t)(n0 + r - kPT) * K;
+      // weight row n: rows of w0 below n_w0, of w1 from there (a 64-column tile never straddles)
+      const int nn = n0 + r - kPT;
+      rowp = nn < n_w0 ? w0 + (size_t)nn * K : w1 + (size_t)(nn - n_w0) * K;
     }
     src[k] = (uint64_t)(uintptr_t)(rowp + (size_t)ch0 * kPK + 8 * lc);
   }
@@ -96,12 +111,39 @@ __global__ __launch_bounds__(256) void proj_partial_bf16_kernel(const uint16_t* 
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(b), acc, 0, 0, 0);
     }
   }
-  // D layout: register r holds row 8 (r / 4) + 4 g + r % 4, column n.  part [split][M][N] fp32
-  float* pp = part + ((size_t)sp * M) * N;
+  // D layout: register r holds row 8 (r / 4) + 4 g + r % 4, column n
+  const int col = n0 + 32 * nh + n;
+  if (splits > 1) {   // fp32 partial [split][M][N], summed by proj_finish_bf16_kernel
+    float* pp = part + ((size_t)sp * M) * N;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 32 * mh + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (m < M) pp[(size_t)m * N + col] = acc[r];
+    }
+    return;
+  }
+  if (n0 < po.rope_from) {   // a plain tile (tiles never straddle rope_from: both are multiples of 64)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 32 * mh + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (m < M) po.y0[(size_t)m * po.ld0 + col] = f2bf(acc[r]);
+    }
+    return;
+  }
+  // a rotary tile: the partner of column n's pair sits in lane n ^ 1 (DPP quad_perm [1, 0, 3, 2])
+  const int c = col - po.rope_from;
+  const int j = (c % po.rope_width) >> 1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
+    const float mine = acc[r];
+    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
     const int m = m0 + 32 * mh + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (m < M) pp[(size_t)m * N + n0 + 32 * nh + n] = acc[r];
+    if (m < M) {
+      const double x0 = (c & 1) ? other : mine, x1 = (c & 1) ? mine : other;
+      double y0, y1;
+      rope_pair(x0, x1, po.positions[m], j, po.rope_width, po.rope_base, &y0, &y1);
+      po.y1[(size_t)m * po.ld1 + c] = d2bf((c & 1) ? y1 : y0);
+    }
   }
 }
 
@@ -134,31 +176,37 @@ __global__ __launch_bounds__(256) void proj_finish_bf16_kernel(const float* __re
   }
 }
 
-// splits of K (in 64-feature chunks) so that about 512 workgroups run, each with at least 4 chunks
+// splits of K (in 64-feature chunks) so that about 256 workgroups run, each with at least 4 chunks;
+// with 256 tiles or more a projection runs unsplit and writes bf16 directly
 int proj_splits(int M, int N, int K) {
   const long long tiles = (long long)((M + kPT - 1) / kPT) * (N / kPT);
   const int chunks = K / kPK;
-  long long s = (512 + tiles - 1) / tiles;
+  long long s = (256 + tiles - 1) / tiles;
   const int max_s = chunks / 4 > 0 ? chunks / 4 : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   return (int)s;
 }
 
-size_t proj_ws_bytes(int M, int N, int K) { return (size_t)proj_splits(M, N, K) * M * N * sizeof(float); }
+size_t proj_ws_bytes(int M, int N, int K) {
+  const int s = proj_splits(M, N, K);
+  return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+}
 
-// y = x W^T (+ RoPE on columns >= rope_from, written to y1); N, K multiples of 64
-hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w, int M, int N, int K, float* part, int rope_from,
-                            int rope_width, const int32_t* positions, float rope_base, uint16_t* y0, int ld0,
-                            uint16_t* y1, int ld1, hipStream_t st) {
+// y = x W^T with W = [w0 (n_w0 rows); w1] (+ RoPE on columns >= rope_from, written to y1);
+// N, n_w0, rope_from and K multiples of 64
+hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* w0, const uint16_t* w1, int n_w0, int M, int N, int K,
+                            float* part, int rope_from, int rope_width, const int32_t* positions, float rope_base,
+                            uint16_t* y0, int ld0, uint16_t* y1, int ld1, hipStream_t st) {
   const int splits = proj_splits(M, N, K);
   const int chunks = K / kPK;
   const int cps = (chunks + splits - 1) / splits;
   const long long tiles = (long long)((M + kPT - 1) / kPT) * (N / kPT);
-  hipLaunchKernelGGL(proj_partial_bf16_kernel, dim3((unsigned)(tiles * splits)), dim3(256), 0, st, x, w, M, N, K,
-                     splits, cps, part);
+  const ProjOut po{y0, ld0, y1, ld1, rope_from, rope_width, positions, (double)rope_base};
+  hipLaunchKernelGGL(proj_partial_bf16_kernel, dim3((unsigned)(tiles * splits)), dim3(256), 0, st, x, w0, w1, n_w0, M,
+                     N, K, splits, cps, part, po);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || splits == 1) return e;
   const long long items = (long long)M * (N / 2);
   hipLaunchKernelGGL(proj_finish_bf16_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st,
                      (const float*)part, M, N, splits, rope_from, rope_width, positions, (double)rope_base, y0, ld0,
