@@ -34,6 +34,14 @@ Readings where the pages are silent (each listed in the design notes):
   * query s of a group of Sq attends cached tokens 0 .. L-Sq+s (itself included).
   * cache rows are rounded to the storage type (bf16: nearest-even).
   * a query that sees no token returns zeros and lse = -inf.
+  * the low-precision latent cache (the pages name quantisation only as a risk,
+    [V2] §5.1 item 3, and fix no format): c^KV is stored as FP8 E4M3 codes
+    (4 exponent bits, bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN,
+    largest finite 448) with one fp32 scale per token, s = amax|c| / 448
+    (s = 1 for an all-zero row), code = round-to-nearest-even(c / s), with the
+    division and the scale in fp32; k^R stays bf16.  The row quantised is the
+    bf16 row a bf16 cache would hold.  A 64-token page stores the 64 latent
+    code rows, then the 64 bf16 rotary rows, then the 64 fp32 scales.
 """
 from __future__ import annotations
 
@@ -46,6 +54,8 @@ __all__ = [
     "q_compress", "layer_queries", "out_project",
     "decode", "decode_absorbed", "latent_elements_per_token", "mha_elements_per_token",
     "mqa_elements_per_token", "gqa_elements_per_token",
+    "e4m3_values", "round_e4m3", "quantize_rows", "dequantize_rows", "fp8_page_bytes",
+    "pack_fp8_pages", "unpack_fp8_pages", "dequantize_pages",
 ]
 
 
@@ -267,3 +277,106 @@ def mqa_elements_per_token(d_head: int) -> int:
 def gqa_elements_per_token(n_groups: int, d_head: int) -> int:
     """n_g shared key/value heads: 2 n_g d_h elements ([V2] §1.2)."""
     return 2 * n_groups * d_head
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache (a reading: the pages fix no low-precision format; [V2] §5.1
+# item 3 names quantisation error as the risk).  Everything here is the format's
+# definition written out; decode over such a cache is ``decode`` applied to the
+# dequantised rows.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """The value of each of the 256 E4M3 codes, from the format's fields: sign
+    bit, 4-bit exponent e (bias 7), 3-bit mantissa m; e = 0 is subnormal
+    (m/8 * 2^-6), e = 15 with m = 7 is NaN (no infinities)."""
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 0xF, code & 0x7
+        if e == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def round_e4m3(y) -> np.ndarray:
+    """E4M3 code of the value nearest to each finite y with |y| <= 448, ties to the
+    code with an even mantissa; the sign bit is y's (so -0.0 and negative values
+    that round to zero give 0x80)."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(~np.isfinite(y)) or np.any(np.abs(y) > E4M3_MAX):
+        raise ValueError("round_e4m3 takes finite values of magnitude <= 448")
+    mags = e4m3_values()[:0x7F]                      # codes 0x00 .. 0x7E, increasing
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)   # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag_code = np.where(pick_hi, hi, lo)
+    return (mag_code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows(rows, d_latent: int):
+    """Quantise cache rows [..., d_latent + d_rope] (values a bf16 cache holds).
+
+    Returns (codes uint8 [..., d_latent], scales float32 [...], rope float64
+    [..., d_rope]): s = fp32(amax / 448) over the row's latent part (1 for an
+    all-zero part), code = round_e4m3(min(max(fp32(c / s), -448), 448))."""
+    rows = np.asarray(rows, dtype=np.float64)
+    lat = rows[..., :d_latent].astype(np.float32)
+    if not np.array_equal(lat.astype(np.float64), rows[..., :d_latent]):
+        raise ValueError("latent values must be representable in fp32")
+    amax = np.max(np.abs(lat), axis=-1)
+    scales = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (lat / scales[..., None]).astype(np.float32)
+    y = np.minimum(np.maximum(y, np.float32(-E4M3_MAX)), np.float32(E4M3_MAX))
+    return round_e4m3(y), scales, rows[..., d_latent:].copy()
+
+
+def dequantize_rows(codes, scales, rope) -> np.ndarray:
+    """Rows [s * value(code) ‖ k^R] in float64 (the products are exact)."""
+    lat = e4m3_values()[np.asarray(codes, dtype=np.int64)] * np.asarray(scales, dtype=np.float64)[..., None]
+    return np.concatenate([lat, np.asarray(rope, dtype=np.float64)], axis=-1)
+
+
+def fp8_page_bytes(block_size: int, d_latent: int, d_rope: int) -> int:
+    """Bytes of one page: block_size x (d_latent code bytes + 2 d_rope bf16 bytes + 4 scale bytes)."""
+    return block_size * (d_latent + 2 * d_rope + 4)
+
+
+def pack_fp8_pages(codes, rope_bf16_bits, scales) -> np.ndarray:
+    """Pages uint8 [num_blocks, page bytes] from codes [nb, bs, d_c] (uint8),
+    rotary rows [nb, bs, d_R] (bf16 bit patterns, uint16) and scales [nb, bs]
+    (float32): the code rows, then the rotary rows, then the scales, each
+    block_size rows long, little-endian."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rope_b = np.ascontiguousarray(rope_bf16_bits, dtype="<u2")
+    sc = np.ascontiguousarray(scales, dtype="<f4")
+    nb = codes.shape[0]
+    return np.concatenate([codes.reshape(nb, -1), rope_b.view(np.uint8).reshape(nb, -1),
+                           sc.view(np.uint8).reshape(nb, -1)], axis=1)
+
+
+def unpack_fp8_pages(pages, block_size: int, d_latent: int, d_rope: int):
+    """Inverse of pack_fp8_pages: (codes, rope bf16 bit patterns, scales)."""
+    pages = np.ascontiguousarray(pages, dtype=np.uint8)
+    nb = pages.shape[0]
+    a = block_size * d_latent
+    b = a + block_size * d_rope * 2
+    codes = pages[:, :a].reshape(nb, block_size, d_latent)
+    rope_bits = pages[:, a:b].copy().view("<u2").reshape(nb, block_size, d_rope)
+    scales = pages[:, b:b + 4 * block_size].copy().view("<f4").reshape(nb, block_size)
+    return codes, rope_bits, scales
+
+
+def dequantize_pages(pages, block_size: int, d_latent: int, d_rope: int) -> np.ndarray:
+    """The float64 pool [nb, block_size, d_latent + d_rope] an FP8 page pool stands for."""
+    codes, rope_bits, scales = unpack_fp8_pages(pages, block_size, d_latent, d_rope)
+    rope = (rope_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return dequantize_rows(codes, scales, rope)

@@ -460,3 +460,122 @@ def pin_layer_queries_rotary(orc) -> float:
 
 ALL_PINS.append(pin_layer_mha_special_case)
 ALL_PINS.append(pin_layer_queries_rotary)
+
+
+# ---------------------------------------------------------------- FP8 latent cache
+def pin_e4m3_table(orc) -> float:
+    """The 256 E4M3 code values equal torch's float8_e4m3fn decoding, and the
+    hand-worked ones: 0x01 = 2^-9 (smallest subnormal), 0x08 = 2^-6 (smallest
+    normal), 0x38 = 1, 0x7E = 448, 0x7F NaN, 0x80 = -0, 0xFE = -448."""
+    import torch
+    mine = orc.e4m3_values()
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if not np.array_equal(mine, lib, equal_nan=True):
+        return math.inf
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+            0x7E: 448.0, 0xFE: -448.0}
+    if any(mine[c] != v for c, v in hand.items()):
+        return math.inf
+    if not (np.isnan(mine[0x7F]) and np.isnan(mine[0xFF]) and mine[0x80] == 0 and np.signbit(mine[0x80])):
+        return math.inf
+    return 0.0
+
+
+def pin_e4m3_rounding(orc) -> float:
+    """Rounding to E4M3 equals torch's float32 -> float8_e4m3fn cast (nearest,
+    ties to even) on log-uniform values from 2^-14 to 448 of both signs and on
+    every midpoint between neighbouring codes; plus hand-worked cases."""
+    import torch
+    rng = _rng(16)
+    mags = orc.e4m3_values()[:0x7F]
+    y = np.exp(rng.uniform(math.log(2.0 ** -14), math.log(448.0), 20000)) * rng.choice([-1.0, 1.0], 20000)
+    mids = (mags[:-1] + mags[1:]) / 2
+    y = np.concatenate([y, mids, -mids, mags, -mags, [0.0, -0.0]]).astype(np.float32)
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if not np.array_equal(orc.round_e4m3(y.astype(np.float64)), lib):
+        return math.inf
+    # 2^-10 sits halfway between 0 and 2^-9 -> 0; 3 * 2^-10 between codes 1 and 2 -> 2;
+    # 1 + 1/16 between 1 (0x38) and 1.125 (0x39) -> 0x38; 1.1875 between 0x39 and 0x3A -> 0x3A;
+    # a tiny negative value rounds to -0 (0x80)
+    hand = orc.round_e4m3(np.array([2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, -1e-5, 447.0, -0.3]))
+    want = np.array([0x00, 0x02, 0x38, 0x3A, 0x80, 0x7E, 0x80 | 0x2A], dtype=np.uint8)   # 0.3 -> 0.3125 = 1.25 * 2^-2
+    return 0.0 if np.array_equal(hand, want) else math.inf
+
+
+def _nearest_code_brute(y: float, vals) -> int:
+    """Code of the finite E4M3 value nearest to y by trying all of them; a tie goes
+    to the code with an even mantissa; the sign follows y."""
+    best, best_d = None, None
+    for code in range(0x7F):
+        d = abs(abs(y) - vals[code])
+        if best is None or d < best_d or (d == best_d and code % 2 == 0):
+            best, best_d = code, d
+    return best | (0x80 if math.copysign(1.0, y) < 0 else 0)
+
+
+def pin_fp8_quantize(orc) -> float:
+    """Row quantisation: (a) a row that is s0 times E4M3 values with a 448 in it
+    (s0 a power of two) comes back exactly; (b) on small random bf16 rows every
+    code equals a brute-force nearest-code search on fp32(c / s) with
+    s = fp32(amax / 448), and |dequantised - c| stays within half a code step
+    (relative 2^-4, absolute 2^-10 s below 2^-6 s) plus the division's rounding;
+    (c) an all-zero row gets scale 1 and zero codes; (d) k^R passes unchanged."""
+    rng = _rng(17)
+    vals = orc.e4m3_values()
+    err = 0.0
+    # (a)
+    for s0 in [2.0 ** -7, 1.0, 2.0 ** 5]:
+        codes = rng.integers(0, 0x7F, 40) | (rng.integers(0, 2, 40) << 7)
+        codes[7] = 0x7E
+        lat = vals[codes] * s0
+        row = np.concatenate([lat, [0.5, -2.0]])[None]
+        c2, sc, rope = orc.quantize_rows(row, 40)
+        deq = orc.dequantize_rows(c2, sc, rope)
+        if sc[0] != np.float32(s0) or not np.array_equal(deq[0, :40], lat) or not np.array_equal(rope[0], [0.5, -2.0]):
+            return math.inf
+    # (b)
+    import torch
+    for trial in range(6):
+        x = torch.from_numpy(rng.standard_normal(12) * np.exp(rng.uniform(-6, 6, 12))).to(torch.bfloat16)
+        x = x.to(torch.float64).numpy()
+        codes, sc, _ = orc.quantize_rows(np.concatenate([x, [1.0]])[None], 12)
+        amax = np.float32(np.max(np.abs(x)))
+        s = np.float32(amax / np.float32(448.0))
+        if sc[0] != s:
+            return math.inf
+        for k in range(12):
+            y = float(np.float32(np.float32(x[k]) / s))
+            y = min(max(y, -448.0), 448.0)
+            if int(codes[0, k]) != _nearest_code_brute(y, vals):
+                return math.inf
+        deq = vals[codes[0]] * float(s)
+        step = np.where(np.abs(x) >= 2.0 ** -6 * float(s), np.abs(x) * 2.0 ** -4, 2.0 ** -10 * float(s))
+        err = max(err, float(np.max(np.abs(deq - x) / (step * (1 + 2.0 ** -20) + 448 * float(s) * 2.0 ** -23))) - 1.0)
+    # (c)
+    codes, sc, _ = orc.quantize_rows(np.zeros((1, 9)), 8)
+    if sc[0] != 1.0 or np.any(codes & 0x7F):
+        return math.inf
+    return max(err, 0.0)
+
+
+def pin_fp8_page_layout(orc) -> float:
+    """A hand-built page (2 tokens, d_c = 2, d_R = 2): code rows, then bf16 rotary
+    rows, then fp32 scales, little-endian; and what it dequantises to."""
+    codes = np.array([[[1, 2], [3, 4]]], dtype=np.uint8)
+    rope_bits = np.array([[[0x3F80, 0x4000], [0xBF80, 0x0000]]], dtype=np.uint16)   # 1, 2, -1, 0
+    scales = np.array([[2.0, 0.5]], dtype=np.float32)
+    want = bytes([1, 2, 3, 4, 0x80, 0x3F, 0x00, 0x40, 0x80, 0xBF, 0x00, 0x00,
+                  0x00, 0x00, 0x00, 0x40, 0x00, 0x00, 0x00, 0x3F])
+    page = orc.pack_fp8_pages(codes, rope_bits, scales)
+    if page.shape != (1, 20) or bytes(page[0]) != want or orc.fp8_page_bytes(2, 2, 2) != 20:
+        return math.inf
+    c2, r2, s2 = orc.unpack_fp8_pages(page, 2, 2, 2)
+    if not (np.array_equal(c2, codes) and np.array_equal(r2, rope_bits) and np.array_equal(s2, scales)):
+        return math.inf
+    # codes 1..4 are the subnormals k * 2^-9
+    rows = orc.dequantize_pages(page, 2, 2, 2)
+    hand = np.array([[[2.0 ** -8, 2.0 ** -7, 1.0, 2.0], [3 * 2.0 ** -10, 2.0 ** -8, -1.0, 0.0]]])
+    return float(np.max(np.abs(rows - hand)))
+
+
+ALL_PINS += [pin_e4m3_table, pin_e4m3_rounding, pin_fp8_quantize, pin_fp8_page_layout]

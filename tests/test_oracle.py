@@ -71,6 +71,21 @@ MUTANTS = {
                         "return qn, rope(qr, np.asarray(positions)[..., None] + 1, rope_base)"),
     "append_without_rope": ("kr = rope(h @ np.asarray(w_kr, dtype=np.float64).T, positions, rope_base)",
                             "kr = h @ np.asarray(w_kr, dtype=np.float64).T"),
+    "e4m3_bias_8": ("vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+                    "vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    "e4m3_subnormal_as_normal": ("vals[code] = sign * (m / 8.0) * 2.0 ** -6",
+                                 "vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** -7"),
+    "e4m3_ties_up": ("pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))",
+                     "pick_hi = (d_hi <= d_lo)"),
+    "e4m3_sign_dropped": ("return (mag_code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)",
+                          "return (mag_code | np.where(y < 0, 0x80, 0)).astype(np.uint8)"),
+    "fp8_scale_int8_range": ("amax / np.float32(E4M3_MAX)", "amax / np.float32(127.0)"),
+    "fp8_scale_not_applied": ("lat = e4m3_values()[np.asarray(codes, dtype=np.int64)] * np.asarray(scales, dtype=np.float64)[..., None]",
+                              "lat = e4m3_values()[np.asarray(codes, dtype=np.int64)] * 1.0"),
+    "fp8_page_rope_after_scales": ("    return np.concatenate([codes.reshape(nb, -1), rope_b.view(np.uint8).reshape(nb, -1),\n"
+                                   "                           sc.view(np.uint8).reshape(nb, -1)], axis=1)",
+                                   "    return np.concatenate([codes.reshape(nb, -1), sc.view(np.uint8).reshape(nb, -1),\n"
+                                   "                           rope_b.view(np.uint8).reshape(nb, -1)], axis=1)"),
 }
 
 
