@@ -37,11 +37,13 @@ Readings where the pages are silent (each listed in the design notes):
   * the low-precision latent cache (the pages name quantisation only as a risk,
     [V2] §5.1 item 3, and fix no format): c^KV is stored as FP8 E4M3 codes
     (4 exponent bits, bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN,
-    largest finite 448) with one fp32 scale per token, s = amax|c| / 448
-    (s = 1 for an all-zero row), code = round-to-nearest-even(c / s), with the
-    division and the scale in fp32; k^R stays bf16.  The row quantised is the
-    bf16 row a bf16 cache would hold.  A 64-token page stores the 64 latent
-    code rows, then the 64 bf16 rotary rows, then the 64 fp32 scales.
+    largest finite 448) with one power-of-two scale per token (the OCP
+    microscaling convention), s = 2^k for the smallest k >= -124 with
+    amax|c| <= 448 s (s = 1 for an all-zero row), code =
+    round-to-nearest-even(c / s), which is exact division; k^R stays bf16.
+    The row quantised is the bf16 row a bf16 cache would hold.  A 64-token
+    page stores the 64 latent code rows, then the 64 bf16 rotary rows, then
+    the 64 scales as fp32.
 """
 from __future__ import annotations
 
@@ -54,7 +56,7 @@ __all__ = [
     "q_compress", "layer_queries", "out_project",
     "decode", "decode_absorbed", "latent_elements_per_token", "mha_elements_per_token",
     "mqa_elements_per_token", "gqa_elements_per_token",
-    "e4m3_values", "round_e4m3", "quantize_rows", "dequantize_rows", "fp8_page_bytes",
+    "e4m3_values", "round_e4m3", "fp8_scale_exponent", "quantize_rows", "dequantize_rows", "fp8_page_bytes",
     "pack_fp8_pages", "unpack_fp8_pages", "dequantize_pages",
 ]
 
@@ -322,21 +324,28 @@ def round_e4m3(y) -> np.ndarray:
     return (mag_code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
 
 
+def fp8_scale_exponent(amax) -> np.ndarray:
+    """k of the per-token scale s = 2^k: the smallest integer k >= -124 with
+    amax <= 448 * 2^k (0 where amax == 0).  amax = m 2^e (frexp, 1/2 <= m < 1)
+    gives amax 2^-(e-9) = 512 m in [256, 512), so k is e - 9 or e - 8."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(amax)
+    k = np.where(512.0 * m <= E4M3_MAX, e - 9, e - 8)
+    k = np.maximum(k, -124)
+    return np.where(amax > 0, k, 0).astype(np.int64)
+
+
 def quantize_rows(rows, d_latent: int):
     """Quantise cache rows [..., d_latent + d_rope] (values a bf16 cache holds).
 
     Returns (codes uint8 [..., d_latent], scales float32 [...], rope float64
-    [..., d_rope]): s = fp32(amax / 448) over the row's latent part (1 for an
-    all-zero part), code = round_e4m3(min(max(fp32(c / s), -448), 448))."""
+    [..., d_rope]): s = 2^k with k from fp8_scale_exponent(amax) over the row's
+    latent part, code = round_e4m3(c / s) (c / s is exact and |c / s| <= 448)."""
     rows = np.asarray(rows, dtype=np.float64)
-    lat = rows[..., :d_latent].astype(np.float32)
-    if not np.array_equal(lat.astype(np.float64), rows[..., :d_latent]):
-        raise ValueError("latent values must be representable in fp32")
-    amax = np.max(np.abs(lat), axis=-1)
-    scales = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    y = (lat / scales[..., None]).astype(np.float32)
-    y = np.minimum(np.maximum(y, np.float32(-E4M3_MAX)), np.float32(E4M3_MAX))
-    return round_e4m3(y), scales, rows[..., d_latent:].copy()
+    lat = rows[..., :d_latent]
+    k = fp8_scale_exponent(np.max(np.abs(lat), axis=-1))
+    y = np.ldexp(lat, -k[..., None])
+    return round_e4m3(y), np.ldexp(1.0, k).astype(np.float32), rows[..., d_latent:].copy()
 
 
 def dequantize_rows(codes, scales, rope) -> np.ndarray:

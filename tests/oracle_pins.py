@@ -515,15 +515,17 @@ def _nearest_code_brute(y: float, vals) -> int:
 
 def pin_fp8_quantize(orc) -> float:
     """Row quantisation: (a) a row that is s0 times E4M3 values with a 448 in it
-    (s0 a power of two) comes back exactly; (b) on small random bf16 rows every
-    code equals a brute-force nearest-code search on fp32(c / s) with
-    s = fp32(amax / 448), and |dequantised - c| stays within half a code step
-    (relative 2^-4, absolute 2^-10 s below 2^-6 s) plus the division's rounding;
-    (c) an all-zero row gets scale 1 and zero codes; (d) k^R passes unchanged."""
+    (s0 a power of two) comes back exactly, with scale s0; (b) on small random
+    bf16 rows the scale is the smallest power of two 2^k (k >= -124) with
+    amax <= 448 * 2^k, found by trying every k, every code equals a brute-force
+    nearest-code search on c / s, and |dequantised - c| stays within half a
+    code step (relative 2^-4, absolute 2^-10 s below 2^-6 s); (c) an all-zero
+    row gets scale 1 and zero codes, a row below the scale floor gets 2^-124;
+    (d) k^R passes unchanged."""
     rng = _rng(17)
     vals = orc.e4m3_values()
     err = 0.0
-    # (a)
+    # (a), (d)
     for s0 in [2.0 ** -7, 1.0, 2.0 ** 5]:
         codes = rng.integers(0, 0x7F, 40) | (rng.integers(0, 2, 40) << 7)
         codes[7] = 0x7E
@@ -535,25 +537,30 @@ def pin_fp8_quantize(orc) -> float:
             return math.inf
     # (b)
     import torch
-    for trial in range(6):
+    for trial in range(8):
         x = torch.from_numpy(rng.standard_normal(12) * np.exp(rng.uniform(-6, 6, 12))).to(torch.bfloat16)
         x = x.to(torch.float64).numpy()
+        if trial == 0:
+            x[3] = 448.0 * 2.0 ** -3          # amax exactly at a boundary: s = 2^-3
+            x[:3] = x[4:] = 0.01
         codes, sc, _ = orc.quantize_rows(np.concatenate([x, [1.0]])[None], 12)
-        amax = np.float32(np.max(np.abs(x)))
-        s = np.float32(amax / np.float32(448.0))
-        if sc[0] != s:
+        amax = float(np.max(np.abs(x)))
+        k = next(k for k in range(-124, 200) if amax <= 448.0 * 2.0 ** k)
+        s = 2.0 ** k
+        if float(sc[0]) != s:
             return math.inf
-        for k in range(12):
-            y = float(np.float32(np.float32(x[k]) / s))
-            y = min(max(y, -448.0), 448.0)
-            if int(codes[0, k]) != _nearest_code_brute(y, vals):
+        for q in range(12):
+            if int(codes[0, q]) != _nearest_code_brute(x[q] / s, vals):
                 return math.inf
-        deq = vals[codes[0]] * float(s)
-        step = np.where(np.abs(x) >= 2.0 ** -6 * float(s), np.abs(x) * 2.0 ** -4, 2.0 ** -10 * float(s))
-        err = max(err, float(np.max(np.abs(deq - x) / (step * (1 + 2.0 ** -20) + 448 * float(s) * 2.0 ** -23))) - 1.0)
+        deq = vals[codes[0]] * s
+        step = np.where(np.abs(x) >= 2.0 ** -6 * s, np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s)
+        err = max(err, float(np.max(np.abs(deq - x) / step)) - 1.0)
     # (c)
     codes, sc, _ = orc.quantize_rows(np.zeros((1, 9)), 8)
     if sc[0] != 1.0 or np.any(codes & 0x7F):
+        return math.inf
+    codes, sc, _ = orc.quantize_rows(np.array([[1e-37, -3e-38, 0.0]]), 2)
+    if float(sc[0]) != 2.0 ** -124 or int(codes[0, 0]) != _nearest_code_brute(1e-37 / 2.0 ** -124, vals):
         return math.inf
     return max(err, 0.0)
 

@@ -79,7 +79,11 @@ MUTANTS = {
                      "pick_hi = (d_hi <= d_lo)"),
     "e4m3_sign_dropped": ("return (mag_code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)",
                           "return (mag_code | np.where(y < 0, 0x80, 0)).astype(np.uint8)"),
-    "fp8_scale_int8_range": ("amax / np.float32(E4M3_MAX)", "amax / np.float32(127.0)"),
+    "fp8_scale_one_binade_low": ("k = np.where(512.0 * m <= E4M3_MAX, e - 9, e - 8)",
+                                 "k = np.where(512.0 * m <= E4M3_MAX, e - 10, e - 9)"),
+    "fp8_scale_boundary": ("k = np.where(512.0 * m <= E4M3_MAX, e - 9, e - 8)",
+                           "k = np.where(512.0 * m < E4M3_MAX, e - 9, e - 8)"),
+    "fp8_scale_no_floor": ("    k = np.maximum(k, -124)\n", "    k = np.maximum(k, -200)\n"),
     "fp8_scale_not_applied": ("lat = e4m3_values()[np.asarray(codes, dtype=np.int64)] * np.asarray(scales, dtype=np.float64)[..., None]",
                               "lat = e4m3_values()[np.asarray(codes, dtype=np.int64)] * 1.0"),
     "fp8_page_rope_after_scales": ("    return np.concatenate([codes.reshape(nb, -1), rope_b.view(np.uint8).reshape(nb, -1),\n"
