@@ -30,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_b64_ctx8192_hbm_traffic.md")
-ATTN_SOURCES = ("mla_rank_latent_amd/csrc/attn_bf16.hip", "mla_rank_latent_amd/csrc/device_util.h",
+ATTN_SOURCES = ("mla_rank_latent_amd/csrc/attn_bf16.hip", "mla_rank_latent_amd/csrc/attn_common.h",
+                "mla_rank_latent_amd/csrc/device_util.h",
                 "mla_rank_latent_amd/csrc/mla_internal.h")
 
 

@@ -20,7 +20,9 @@
  *    launch is asynchronous on the caller's stream (`stream` is a hipStream_t,
  *    NULL = the default stream).
  *  - Arrays are dense, row-major, in the element type named by dims->dtype
- *    (MLA_DTYPE_F32: float, MLA_DTYPE_BF16: bfloat16) unless typed int32/float.
+ *    (MLA_DTYPE_F32: float, MLA_DTYPE_BF16 and MLA_DTYPE_BF16_FP8: bfloat16)
+ *    unless typed int32/float; with MLA_DTYPE_BF16_FP8 the cache alone is in
+ *    the FP8 page format described below.
  *    Device arrays must be 16-byte aligned.
  *  - Weights are stored out x in, as the page writes W in R^{out x in}.
  *  - Problems that only the data can reveal (a block id outside the pool, a
@@ -51,15 +53,39 @@ extern "C" {
 #define MLA_ERR_WORKSPACE_TOO_SMALL  -5  /* workspace_bytes < mla_decode_workspace_bytes(...) */
 #define MLA_ERR_CAPACITY             -6  /* a size exceeds what the kernels index (see below) */
 #define MLA_ERR_HIP                  -7  /* the HIP runtime refused a launch */
-#define MLA_ERR_UNSUPPORTED          -8  /* valid dims that the bf16 kernels are not built for */
+#define MLA_ERR_UNSUPPORTED          -8  /* valid dims or dtype this entry point is not built for */
 
 /* bits OR-ed into *status by the kernels */
 #define MLA_STATUS_BAD_BLOCK   0x1  /* block_table named a block outside [0, num_blocks) */
 #define MLA_STATUS_BAD_LENGTH  0x2  /* seq_lens[b] < sq or > max_blocks * block_size */
 #define MLA_STATUS_BAD_POS     0x4  /* append position < 0 or >= max_blocks * block_size */
 
-#define MLA_DTYPE_F32   0
-#define MLA_DTYPE_BF16  1
+#define MLA_DTYPE_F32       0
+#define MLA_DTYPE_BF16      1
+#define MLA_DTYPE_BF16_FP8  2   /* bf16 tensors, latent cache in FP8 E4M3 pages */
+
+/*
+ * The FP8 latent cache (MLA_DTYPE_BF16_FP8).  The "DeepSeek-V2 ... MLA" page
+ * §5.1 (item 3) names quantisation error as the risk of a low-precision form
+ * and fixes no format; this library's format:
+ *  - c^KV is stored as OCP FP8 E4M3 codes (bias 7, 3 mantissa bits, no
+ *    infinities, largest finite 448) with one power-of-two scale per token,
+ *    s = 2^k for the smallest k >= -124 with max_i |c_i| <= 448 s (s = 1 for an
+ *    all-zero c), code_i = round-to-nearest-even(c_i / s) (an exact division;
+ *    the sign of zero is kept).  The value a code stands for is s * e4m3(code),
+ *    exactly a bfloat16 value for rows with max |c_i| < 2^127.
+ *  - k^R stays bfloat16.
+ *  - What is quantised is the bf16 row [c ‖ k^R] a MLA_DTYPE_BF16 cache holds,
+ *    so an FP8 cache equals mla_cache_quantize() of the bf16 cache.
+ *  - Block size 64.  Page b (MLA_FP8_PAGE_BYTES bytes) holds the 64 rows of
+ *    512 codes (bytes [0, 32768)), then the 64 k^R rows of 64 bf16
+ *    ([32768, 40960)), then the 64 scales as little-endian fp32 ([40960, 41216)).
+ *    A cache of num_blocks pages is num_blocks * MLA_FP8_PAGE_BYTES bytes.
+ *  - Decode computes on the dequantised values s * e4m3(code) exactly (the
+ *    products see the same bfloat16 values a bf16 cache of those values would
+ *    hold), so results match the bf16 path on the dequantised cache.
+ */
+#define MLA_FP8_PAGE_BYTES 41216
 
 /* Model dimensions (names follow the DeepSeek-V2 MLA page's notation). */
 typedef struct mla_dims {
@@ -75,7 +101,8 @@ typedef struct mla_dims {
 
 /*
  * Size limits.
- *  - MLA_DTYPE_BF16 runs the MFMA kernels, built for DeepSeek-V2's widths:
+ *  - MLA_DTYPE_BF16 and MLA_DTYPE_BF16_FP8 run the MFMA kernels, built for
+ *    DeepSeek-V2's widths:
  *    d_nope = 128, d_rope = 64, d_latent = 512, block_size = 64, n_heads in
  *    1..1024, d_model a multiple of 32, sq in 1..8.  Other bf16 dims give
  *    MLA_ERR_UNSUPPORTED (sq above 8: MLA_ERR_CAPACITY).
@@ -91,8 +118,9 @@ const char* mla_status_str(int code);
 /*
  * Bytes the latent cache needs for `tokens` tokens: tokens * (d_latent + d_rope)
  * * sizeof(dtype) ("DeepSeek-V2 ... MLA" page §3.3: d_c + d_h^R elements per
- * token per layer, against MHA's 2 n_h d_h in §1.1).  Returns 0 for invalid dims
- * or a negative token count.  Pure host arithmetic.
+ * token per layer, against MHA's 2 n_h d_h in §1.1); for MLA_DTYPE_BF16_FP8,
+ * whole pages: ceil(tokens / 64) * MLA_FP8_PAGE_BYTES.  Returns 0 for invalid
+ * dims or a negative token count.  Pure host arithmetic.
  */
 size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens);
 
@@ -129,6 +157,10 @@ size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens);
  *            differ in the last bit, because they sum in different orders.
  * status     optional int32 (device), OR-ed with MLA_STATUS_BAD_POS/BAD_BLOCK; a
  *            row whose position or block is invalid is skipped.
+ * MLA_DTYPE_BF16_FP8: cache is the FP8 page pool; the bf16 row is computed as
+ * above (the split or GEMM path), written to the workspace, then quantised into
+ * its page slot.  The workspace is required (mla_cache_append_workspace_bytes;
+ * MLA_ERR_WORKSPACE_TOO_SMALL without it).
  */
 int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr,
                      const int32_t* positions, const int32_t* block_table, int32_t max_blocks,
@@ -140,6 +172,17 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
  * 0 when the path needs none (fp32) or the arguments are invalid.
  */
 size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t t);
+
+/*
+ * Quantise a whole bf16 cache into the FP8 page format (the format described
+ * at MLA_DTYPE_BF16_FP8): page b of `pages` from block b of `src`, for
+ * b < num_blocks.  dims->dtype must be MLA_DTYPE_BF16_FP8 (MLA_ERR_BAD_DTYPE
+ * otherwise) and the other dims the MFMA kernels' widths.
+ *
+ * src        [num_blocks, 64, 576]             bfloat16, finite (device)
+ * pages      [num_blocks, MLA_FP8_PAGE_BYTES]  bytes, written (device)
+ */
+int mla_cache_quantize(const mla_dims* dims, const void* src, void* pages, int32_t num_blocks, void* stream);
 
 /*
  * Project the query hidden states of `sq` tokens per sequence:
@@ -178,6 +221,7 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s
  * q_rope     [batch, sq, n_heads, d_rope]   dtype, already rotated
  * w_uk, w_uv [n_heads*d_nope, d_latent]     dtype
  * cache      [num_blocks, block_size, d_latent + d_rope]  dtype
+ *            (MLA_DTYPE_BF16_FP8: [num_blocks, MLA_FP8_PAGE_BYTES] pages)
  * block_table[batch, max_blocks]            int32 (device)
  * seq_lens   [batch]                        int32 (device), query tokens included
  * softmax_scale  e.g. 1/sqrt(d_nope + d_rope)
@@ -234,7 +278,7 @@ int mla_decode_finish(const mla_dims* dims, const void* q_nope, const void* q_ro
  * §2.3 query compression; "【深度学习】DeepSeek焦点架构-MLA" page 02 (3) and
  * (5): the compressed query's up-projections give each head's q^C and its
  * rotary q^R, and the heads' outputs, concatenated, pass through W^O).
- * bf16 only (f32: MLA_ERR_UNSUPPORTED); d_model and d_qlat multiples of 64;
+ * bf16 tensors only (f32: MLA_ERR_UNSUPPORTED); d_model and d_qlat multiples of 64;
  * batch * sq <= 2^20.  Products accumulate in fp32, split over the input
  * features across workgroups and summed in a fixed order, so results do not
  * depend on timing.
@@ -293,7 +337,7 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t 
  * workspace  device scratch of at least mla_prefill_workspace_bytes(dims,
  *            batch, max_blocks) bytes, 256-byte aligned; clobbered
  * out        [batch, t, n_heads, d_nope]   bf16
- * Limits: bf16 dims only (f32: MLA_ERR_UNSUPPORTED);
+ * Limits: MLA_DTYPE_BF16 only (f32 and the FP8 cache: MLA_ERR_UNSUPPORTED);
  * max_blocks * block_size <= 2^23.
  */
 int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope,

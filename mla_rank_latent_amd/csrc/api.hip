@@ -16,17 +16,21 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t elem_size(int dtype) { return dtype == MLA_DTYPE_BF16 ? 2 : 4; }
+// bf16 tensors: MLA_DTYPE_BF16, and MLA_DTYPE_BF16_FP8 (which differs only in the cache)
+bool is_bf(const mla_dims* d) { return d->dtype == MLA_DTYPE_BF16 || d->dtype == MLA_DTYPE_BF16_FP8; }
+bool is_fp8(const mla_dims* d) { return d->dtype == MLA_DTYPE_BF16_FP8; }
+size_t elem_size(int dtype) { return dtype == MLA_DTYPE_F32 ? 4 : 2; }
 
 // Checks that hold for every entry point.
 int check_dims(const mla_dims* d) {
   if (d == nullptr) return MLA_ERR_NULL_PTR;
-  if (d->dtype != MLA_DTYPE_F32 && d->dtype != MLA_DTYPE_BF16) return MLA_ERR_BAD_DTYPE;
+  if (d->dtype != MLA_DTYPE_F32 && d->dtype != MLA_DTYPE_BF16 && d->dtype != MLA_DTYPE_BF16_FP8)
+    return MLA_ERR_BAD_DTYPE;
   if (d->n_heads < 1 || d->d_nope < 1 || d->d_rope < 0 || d->d_latent < 1 || d->d_model < 1 || d->block_size < 1)
     return MLA_ERR_BAD_DIMS;
   if (d->d_rope % 2 != 0) return MLA_ERR_BAD_DIMS;   // RoPE turns pairs
   if (!(d->rope_base > 0.0f) || !std::isfinite(d->rope_base)) return MLA_ERR_BAD_DIMS;
-  if (d->dtype == MLA_DTYPE_BF16) {
+  if (is_bf(d)) {
     if (d->d_nope != kNope || d->d_rope != kRope || d->d_latent != kLat || d->block_size != kBlk)
       return MLA_ERR_UNSUPPORTED;
     if (d->n_heads > 1024 || d->d_model % 32 != 0) return MLA_ERR_UNSUPPORTED;
@@ -41,7 +45,7 @@ int check_dims(const mla_dims* d) {
 
 int check_sq(const mla_dims* d, int sq) {
   if (sq < 1) return MLA_ERR_BAD_DIMS;
-  if (sq > (d->dtype == MLA_DTYPE_BF16 ? kMaxSqBf16 : kF32MaxSq)) return MLA_ERR_CAPACITY;
+  if (sq > (is_bf(d) ? kMaxSqBf16 : kF32MaxSq)) return MLA_ERR_CAPACITY;
   if (d->dtype == MLA_DTYPE_F32 && d->n_heads * sq > 65535) return MLA_ERR_CAPACITY;   // one grid row per query row
   return MLA_OK;
 }
@@ -75,7 +79,7 @@ int device_cu_count() {
 }
 
 bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L) {
-  const bool bf = d->dtype == MLA_DTYPE_BF16;
+  const bool bf = is_bf(d);
   if (bf) {
     L->hg = d->n_heads < kRowsWG / sq ? d->n_heads : kRowsWG / sq;
     L->G = (d->n_heads + L->hg - 1) / L->hg;
@@ -125,26 +129,33 @@ const char* mla_status_str(int code) {
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_decode_workspace_bytes()";
     case MLA_ERR_CAPACITY: return "a size exceeds what the kernels can index";
     case MLA_ERR_HIP: return "the HIP runtime refused a launch";
-    case MLA_ERR_UNSUPPORTED: return "dims the bf16 kernels are not built for";
+    case MLA_ERR_UNSUPPORTED: return "dims or an element type this entry point is not built for";
     default: return "unknown status code";
   }
 }
 
 size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens) {
   if (check_dims(dims) != MLA_OK || tokens < 0) return 0;
+  if (is_fp8(dims)) return (size_t)((tokens + kBlk - 1) / kBlk) * kFp8PageBytes;   // whole pages
   return (size_t)tokens * ((size_t)dims->d_latent + dims->d_rope) * elem_size(dims->dtype);
 }
 
 namespace {
 bool append_uses_gemm(const mla_dims* d, long long tokens) {
-  return d->dtype == MLA_DTYPE_BF16 && tokens >= kAppendGemmMinTokens && d->d_model % 64 == 0;
+  return is_bf(d) && tokens >= kAppendGemmMinTokens && d->d_model % 64 == 0;
 }
+// FP8 append: the bf16 rows are first written densely to the workspace, then quantised into
+// their pages; the split path's partial products follow the staging rows
+size_t fp8_staging_bytes(long long tokens) { return up((size_t)tokens * kRow * 2); }
 }  // namespace
 
 size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t t) {
   if (check_dims(dims) != MLA_OK || batch < 1 || t < 1 || (long long)batch * t >= (1ll << 30)) return 0;
-  if (dims->dtype != MLA_DTYPE_BF16 || append_uses_gemm(dims, (long long)batch * t)) return 0;
-  return append_split_ws_bytes(dims->d_model, (long long)batch * t);
+  const long long tokens = (long long)batch * t;
+  const size_t split = append_uses_gemm(dims, tokens) ? 0 : append_split_ws_bytes(dims->d_model, tokens);
+  if (is_fp8(dims)) return fp8_staging_bytes(tokens) + split;
+  if (dims->dtype != MLA_DTYPE_BF16) return 0;
+  return split;
 }
 
 int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr, const int32_t* positions,
@@ -160,10 +171,29 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
       !aligned16(cache) || (status && ((uintptr_t)status & 3u)) || (workspace && !aligned16(workspace)))
     return MLA_ERR_BAD_ALIGN;
   const bool gemm = append_uses_gemm(dims, (long long)batch * t);
+  hipStream_t st = (hipStream_t)stream;
+  if (is_fp8(dims)) {
+    // bf16 rows into the workspace (dense, row = token), then quantised into their pages
+    const long long tokens = (long long)batch * t;
+    if (workspace == nullptr || workspace_bytes < mla_cache_append_workspace_bytes(dims, batch, t))
+      return MLA_ERR_WORKSPACE_TOO_SMALL;
+    uint16_t* rows = (uint16_t*)workspace;
+    float* part = (float*)((uint8_t*)workspace + fp8_staging_bytes(tokens));
+    hipError_t e =
+        gemm ? launch_append_gemm_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions,
+                                       nullptr, max_blocks, rows, num_blocks, batch * t, t, dims->d_model,
+                                       dims->rope_base, status, st)
+             : launch_append_split_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions,
+                                        nullptr, max_blocks, rows, num_blocks, batch * t, t, dims->d_model,
+                                        dims->rope_base, part, status, st);
+    if (e == hipSuccess)
+      e = launch_quant_rows_fp8(rows, tokens, positions, block_table, max_blocks, t, num_blocks, (uint8_t*)cache,
+                                status, st);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
   const bool split = !gemm && workspace != nullptr && dims->dtype == MLA_DTYPE_BF16;
   if (split && workspace_bytes < append_split_ws_bytes(dims->d_model, (long long)batch * t))
     return MLA_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (gemm)
     e = launch_append_gemm_bf16((const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr, positions,
@@ -183,12 +213,25 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_cache_quantize(const mla_dims* dims, const void* src, void* pages, int32_t num_blocks, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if (!is_fp8(dims)) return MLA_ERR_BAD_DTYPE;
+  if (!src || !pages) return MLA_ERR_NULL_PTR;
+  if (num_blocks < 1) return MLA_ERR_BAD_DIMS;
+  if ((long long)num_blocks * kBlk >= (1ll << 31)) return MLA_ERR_CAPACITY;
+  if (!aligned16(src) || !aligned16(pages)) return MLA_ERR_BAD_ALIGN;
+  hipError_t e = launch_quant_rows_fp8((const uint16_t*)src, (long long)num_blocks * kBlk, nullptr, nullptr, 0, 1,
+                                       num_blocks, (uint8_t*)pages, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 namespace {
 // the full layer's projections run on bf16 tiles of 64 features (d_qlat 0: not used by the call)
 int check_layer(const mla_dims* d, int d_qlat, int batch, int sq) {
   int rc = check_dims(d);
   if (rc != MLA_OK) return rc;
-  if (d->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!is_bf(d)) return MLA_ERR_UNSUPPORTED;
   if (d_qlat != 0 && (d_qlat < 64 || d_qlat % 64 != 0)) return MLA_ERR_UNSUPPORTED;
   if (d->d_model % 64 != 0) return MLA_ERR_UNSUPPORTED;
   if (d_qlat > (1 << 16)) return MLA_ERR_CAPACITY;
@@ -302,13 +345,15 @@ int decode_phases(int phases, const mla_dims* dims, const void* q_nope, const vo
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   hipError_t e = hipSuccess;
-  if (dims->dtype == MLA_DTYPE_BF16) {
+  if (is_bf(dims)) {
     if (phases & kPhasePrepare)
       e = launch_absorb_bf16(L, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens,
                              max_blocks, batch, sq, dims->n_heads, ws, status, st);
     if (e == hipSuccess && (phases & kPhaseAttend))
-      e = launch_attn_bf16(L, (const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq,
-                           dims->n_heads, softmax_scale, ws, status, st);
+      e = is_fp8(dims) ? launch_attn_fp8(L, (const uint8_t*)cache, num_blocks, block_table, max_blocks, seq_lens,
+                                         batch, sq, dims->n_heads, softmax_scale, ws, status, st)
+                       : launch_attn_bf16(L, (const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens,
+                                          batch, sq, dims->n_heads, softmax_scale, ws, status, st);
     if (e == hipSuccess && (phases & kPhaseFinish))
       e = launch_merge_upv_bf16(L, (const uint16_t*)w_uv, batch, sq, dims->n_heads, ws, (uint16_t*)out, lse, st);
   } else {

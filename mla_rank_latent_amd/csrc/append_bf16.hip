@@ -21,6 +21,25 @@ namespace mla {
 namespace {
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 constexpr int kAppendWaves = 16;
+
+// Where token tok's row goes: its paged slot (block_table[b][pos / 64], pos % 64),
+// or, with no block table, row tok of a dense [tokens][576] array (the staging
+// rows the FP8 cache path quantises, which checks positions and blocks itself).
+// Null, after reporting, for a position or block outside its table row.
+__device__ __forceinline__ uint16_t* append_dst(uint16_t* cache, const int32_t* block_table, int max_blocks,
+                                                int num_blocks, int tok, int t_per_seq, int pos, int32_t* status) {
+  if (block_table == nullptr) return cache + (size_t)tok * kRow;
+  if (pos < 0 || pos >= max_blocks * kBlk) {
+    if (status) atomicOr(status, MLA_STATUS_BAD_POS);
+    return nullptr;
+  }
+  const int blk = block_table[(size_t)(tok / t_per_seq) * max_blocks + pos / kBlk];
+  if (blk < 0 || blk >= num_blocks) {
+    if (status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
+    return nullptr;
+  }
+  return cache + ((size_t)blk * kBlk + pos % kBlk) * kRow;
+}
 }  // namespace
 
 __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
@@ -74,17 +93,9 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
     const int tok = tb * 16 + row;
     const int col = cb * 16 + cl;
     if (tok < tokens) {
-      const int b = tok / t_per_seq;
       const int pos = positions[tok];
-      if (pos < 0 || pos >= max_blocks * kBlk) {
-        if (status) atomicOr(status, MLA_STATUS_BAD_POS);
-        return;
-      }
-      const int blk = block_table[(size_t)b * max_blocks + pos / kBlk];
-      if (blk < 0 || blk >= num_blocks) {
-        if (status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
-        return;
-      }
+      uint16_t* dst = append_dst(cache, block_table, max_blocks, num_blocks, tok, t_per_seq, pos, status);
+      if (dst == nullptr) return;
       uint16_t outv;
       if (col < kLat) {
         outv = f2bf(v);
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
         rope_pair(x0, x1, pos, j >> 1, kRope, rope_base, &y0, &y1);
         outv = d2bf((j & 1) ? y1 : y0);
       }
-      cache[((size_t)blk * kBlk + pos % kBlk) * kRow + col] = outv;
+      dst[col] = outv;
     }
   }
 }
@@ -214,17 +225,9 @@ __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __
         v1 += p[u].y;
       }
   }
-  const int b = tok / t_per_seq;
   const int pos = positions[tok];
-  if (pos < 0 || pos >= max_blocks * kBlk) {
-    if (status) atomicOr(status, MLA_STATUS_BAD_POS);
-    return;
-  }
-  const int blk = block_table[(size_t)b * max_blocks + pos / kBlk];
-  if (blk < 0 || blk >= num_blocks) {
-    if (status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
-    return;
-  }
+  uint16_t* dst = append_dst(cache, block_table, max_blocks, num_blocks, tok, t_per_seq, pos, status);
+  if (dst == nullptr) return;
   uint32_t outv;
   if (col < kLat) {
     outv = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __
     rope_pair((double)v0, (double)v1, pos, (col - kLat) >> 1, kRope, rope_base, &y0, &y1);
     outv = (uint32_t)d2bf(y0) | ((uint32_t)d2bf(y1) << 16);
   }
-  *(uint32_t*)(cache + ((size_t)blk * kBlk + pos % kBlk) * kRow + col) = outv;
+  *(uint32_t*)(dst + col) = outv;
 }
 
 // ---------------------------------------------------------------------------
@@ -361,17 +364,9 @@ __global__ __launch_bounds__(256) void append_gemm_bf16_kernel(
     if (tok >= tokens) continue;
     const float v0 = tile[row * kGN + cp], v1 = tile[row * kGN + cp + 1];
     const int col = n0 + cp;
-    const int b = tok / t_per_seq;
     const int pos = positions[tok];
-    if (pos < 0 || pos >= max_blocks * kBlk) {
-      if (status) atomicOr(status, MLA_STATUS_BAD_POS);
-      continue;
-    }
-    const int blk = block_table[(size_t)b * max_blocks + pos / kBlk];
-    if (blk < 0 || blk >= num_blocks) {
-      if (status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
-      continue;
-    }
+    uint16_t* dst = append_dst(cache, block_table, max_blocks, num_blocks, tok, t_per_seq, pos, status);
+    if (dst == nullptr) continue;
     uint32_t outv;
     if (col < kLat) {
       outv = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
@@ -380,7 +375,7 @@ __global__ __launch_bounds__(256) void append_gemm_bf16_kernel(
       rope_pair((double)v0, (double)v1, pos, (col - kLat) >> 1, kRope, rope_base, &y0, &y1);
       outv = (uint32_t)d2bf(y0) | ((uint32_t)d2bf(y1) << 16);
     }
-    *(uint32_t*)(cache + ((size_t)blk * kBlk + pos % kBlk) * kRow + col) = outv;
+    *(uint32_t*)(dst + col) = outv;
   }
 }
 

@@ -42,11 +42,12 @@
 //    score seen (exact; for real logit spreads it never happens).  O is never
 //    rescaled in registers, so its accumulators are written only by MFMAs
 //    and stay in AGPRs.
-#include "device_util.h"
+#include "attn_common.h"
 
 namespace mla {
 
 namespace {
+using namespace attn;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyTau = 16.0f;   // p = 2^(z - reference) stays <= 2^16
@@ -57,61 +58,7 @@ constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;   // 9 copies of 1 KB
 constexpr int kPfS = 4;   // score operands read ahead
 constexpr int kPfO = 5;   // PV operands read ahead
 
-#define MLA_CONST __attribute__((address_space(4)))
-// Read-only tables go through the constant address space so that wave-uniform
-// lookups become scalar loads (counted by lgkmcnt, never waiting on the
-// in-flight tile copies, which are counted by vmcnt).
-template <typename T>
-__device__ __forceinline__ const MLA_CONST T* as_const(const T* p) {
-  return (const MLA_CONST T*)p;
-}
-
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
-
-__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Score MFMAs with their accumulators in VGPRs (the latent accumulators fill the
-// AGPRs).  Written as asm so that the choice is per instruction; the hazards
-// the compiler would otherwise handle are handled here: a chain starts from a
-// literal zero (no vector write precedes it), a chain accumulates in place with
-// the same opcode (back-to-back dependent issue is supported), and the results
-// are read only after settle_s's wait states.
-__device__ __forceinline__ void mfma_s_first(f32x16& acc, u32x4 a, u32x4 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_s(f32x16& acc, u32x4 a, u32x4 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-// 24 wait states: more than an 8- or 16-pass MFMA's result needs before a vector read
-__device__ __forceinline__ void settle_s(f32x16& a0, f32x16& a1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
-}
-
-__device__ __forceinline__ u32x4 lds_read16(const MLA_LDS uint8_t* p) { return *(const MLA_LDS u32x4*)p; }
-
-__device__ __forceinline__ u32x2 lds_read_tr(const MLA_LDS uint8_t* p) {
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// One 16-byte-per-lane copy HBM -> LDS: global address = base + voff, LDS
-// address = m0 + 16 * lane.  Issued as asm so that the compiler does not
-// treat every later LDS read as aliasing the copy (it would then wait for all
-// copies in flight); the ring protocol waits for exactly the stage it reads.
-// The cache stream is read once, so it is marked non-temporal: it then
-// displaces less of what the step's other kernels re-read from the caches.
-__device__ __forceinline__ void copy16_to_lds(uint64_t base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds_addr)
-               : "memory");
-}
-
-// a wave-uniform 64-bit address, made visibly uniform (scalar registers)
-__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
 
 }  // namespace
 
@@ -392,8 +339,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
           const int fb = j & 15, hs = j >> 4;
           const int o0 = (o_off[fb & 1] ^ (16 * (4 * hs))) + (fb >> 1) * 128 + (16 * hs) * (kRow * 2);
           const int o1 = (o_off[fb & 1] ^ (16 * (4 * hs + 2))) + (fb >> 1) * 128 + (16 * hs + 8) * (kRow * 2);
-          const u32x2 lo2 = lds_read_tr(sto + o0);
-          const u32x2 hi2 = lds_read_tr(sto + o1);
+          const u32x2 lo2 = lds_read_tr16(sto + o0);
+          const u32x2 hi2 = lds_read_tr16(sto + o1);
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         };
         u32x4 av[kPfO];

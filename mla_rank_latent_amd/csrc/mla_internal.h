@@ -24,6 +24,11 @@ constexpr int kStages = 4;           // LDS ring depth
 constexpr int kStageBytes = kSubTok * kRow * 2;        // 36864
 constexpr int kChunksPerRow = kRow * 2 / 16;           // 72 chunks of 16 B
 constexpr int kMaxSqBf16 = 8;
+// FP8 latent cache page (MLA_DTYPE_BF16_FP8): 64 rows of E4M3 codes, then 64 bf16
+// k^R rows, then 64 fp32 scales
+constexpr int kFp8RopeOff = kBlk * kLat;                       // 32768
+constexpr int kFp8ScaleOff = kFp8RopeOff + kBlk * kRope * 2;   // 40960
+constexpr int kFp8PageBytes = kFp8ScaleOff + kBlk * 4;         // 41216
 
 // f32 generic path limits
 constexpr int kF32MaxWidth = 1024;
@@ -83,6 +88,15 @@ hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_bl
                             const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
                             int batch, int sq, int n_heads, float scale, uint8_t* ws, int32_t* status,
                             hipStream_t st);
+hipError_t launch_attn_fp8(const WsLayout& L, const uint8_t* pages, int num_blocks, const int32_t* block_table,
+                           int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float scale,
+                           uint8_t* ws, int32_t* status, hipStream_t st);
+// FP8 cache rows: quantise bf16 rows [n_rows][576] into pages.  positions == null: row r is
+// slot r % 64 of page r / 64 (a whole pool); otherwise token r goes to its position's slot
+// (t_per_seq tokens per sequence), invalid positions and blocks reported and skipped.
+hipError_t launch_quant_rows_fp8(const uint16_t* src, long long n_rows, const int32_t* positions,
+                                 const int32_t* block_table, int max_blocks, int t_per_seq, int num_blocks,
+                                 uint8_t* pages, int32_t* status, hipStream_t st);
 hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads,
                                  uint8_t* ws, uint16_t* out, float* lse, hipStream_t st);
 // many-token append (prefill chunks): one GEMM kernel, no workspace; used for bf16 when

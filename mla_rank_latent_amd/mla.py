@@ -17,11 +17,15 @@ LIB_PATH = os.path.join(HERE, "libmla_rank_latent.so")
 
 MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
+MLA_DTYPE_BF16_FP8 = 2   # bf16 tensors, latent cache in FP8 E4M3 pages
+MLA_FP8_PAGE_BYTES = 41216
+_DTYPES = {"f32": MLA_DTYPE_F32, "bf16": MLA_DTYPE_BF16, "bf16_fp8": MLA_DTYPE_BF16_FP8}
 MLA_STATUS_BAD_BLOCK = 0x1
 MLA_STATUS_BAD_LENGTH = 0x2
 MLA_STATUS_BAD_POS = 0x4
 
 EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_append_workspace_bytes",
+           "mla_cache_quantize",
            "mla_q_project", "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
            "mla_decode_finish", "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_expand",
            "mla_prefill_attend", "mla_layer_workspace_bytes", "mla_q_compress", "mla_out_project")
@@ -59,6 +63,8 @@ _lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _
                                   _P, _P]
 _lib.mla_cache_append_workspace_bytes.restype = ctypes.c_size_t
 _lib.mla_cache_append_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I]
+_lib.mla_cache_quantize.restype = ctypes.c_int
+_lib.mla_cache_quantize.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _I, _P]
 _lib.mla_q_project.restype = ctypes.c_int
 _lib.mla_q_project.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I, _I, _P]
 _lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -90,8 +96,8 @@ class MlaError(RuntimeError):
 
 def dims(n_heads: int, d_nope: int, d_rope: int, d_latent: int, d_model: int, block_size: int = 64,
          dtype: str = "bf16", rope_base: float = 10000.0) -> MlaDims:
-    return MlaDims(n_heads, d_nope, d_rope, d_latent, d_model, block_size,
-                   MLA_DTYPE_BF16 if dtype == "bf16" else MLA_DTYPE_F32, rope_base)
+    """dtype: "bf16", "f32", or "bf16_fp8" (bf16 tensors, the cache in FP8 pages)."""
+    return MlaDims(n_heads, d_nope, d_rope, d_latent, d_model, block_size, _DTYPES[dtype], rope_base)
 
 
 def _ptr(t) -> Optional[int]:
@@ -181,6 +187,13 @@ def mla_cache_append(d: MlaDims, h, w_dkv, w_kr, positions, block_table, cache, 
         ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(positions), _ptr(block_table),
         int(block_table.shape[1]), _ptr(cache), int(cache.shape[0]), batch, t, _ptr(workspace), _nbytes(workspace),
         _ptr(status), _stream(stream)))
+
+
+def mla_cache_quantize(d: MlaDims, src, pages, stream=None) -> None:
+    """src [num_blocks, 64, d_latent + d_rope] bf16 -> pages [num_blocks, MLA_FP8_PAGE_BYTES] uint8 (written);
+    ``d`` has dtype "bf16_fp8"."""
+    _check("mla_cache_quantize", _lib.mla_cache_quantize(ctypes.byref(d), _ptr(src), _ptr(pages),
+                                                         int(src.shape[0]), _stream(stream)))
 
 
 def mla_q_project(d: MlaDims, h, w_q, w_qr, positions, q_nope, q_rope, stream=None) -> None:

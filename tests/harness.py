@@ -31,24 +31,55 @@ def host(t) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def mla_dims(spec: synth.Spec):
+def mla_dims(spec: synth.Spec, cache: str = ""):
+    """Library dims for a generated workload; cache="fp8" selects the FP8 page cache."""
     from mla_rank_latent_amd import mla
-    return mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, spec.dtype,
+    dtype = "bf16_fp8" if cache == "fp8" else spec.dtype
+    return mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, dtype,
                     spec.rope_base)
+
+
+def fp8_pages(pool_bits: np.ndarray, d_latent: int) -> np.ndarray:
+    """The oracle's FP8 pages [nb, page bytes] for a bf16 pool (bit patterns [nb, 64, R])."""
+    codes, scales, _ = mla_oracle.quantize_rows(synth.as_float(pool_bits, "bf16"), d_latent)
+    return mla_oracle.pack_fp8_pages(codes, pool_bits[..., d_latent:], scales)
+
+
+def with_fp8_cache(x: dict, pages: bool = True) -> dict:
+    """A copy of generated inputs whose cache is FP8.  The oracle then reads every block as
+    its own quantisation of the bf16 block, dequantised; ``pages`` (what the GPU is handed)
+    is the oracle's quantisation of the whole pool."""
+    x8 = dict(x)
+    x8["fp8"] = True
+    if pages:
+        x8["pages"] = fp8_pages(x["pool"], x["spec"].d_latent)
+    return x8
+
+
+def pool_blocks(x: dict, blocks) -> np.ndarray:
+    """float64 values the oracle reads for the given cache blocks (for an FP8 cache: the
+    oracle's quantisation of those bf16 blocks, dequantised)."""
+    spec = x["spec"]
+    blk = x["pool"][np.asarray(blocks)]
+    if x.get("fp8"):
+        return mla_oracle.dequantize_pages(fp8_pages(blk, spec.d_latent), spec.block_size, spec.d_latent,
+                                           spec.d_rope)
+    return synth.as_float(blk, spec.dtype)
 
 
 class GpuCase:
     """Device copies of one generated workload, plus the calls of one decode step."""
     split_append = True    # append through the workspace (split) path
 
-    def __init__(self, x: dict, num_splits: int = 0):
+    def __init__(self, x: dict, num_splits: int = 0, cache: str = ""):
         import torch
         from mla_rank_latent_amd import mla
         self.x = x
         self.spec = spec = x["spec"]
-        self.d = mla_dims(spec)
+        self.cache = cache
+        self.d = mla_dims(spec, cache)
         self.num_splits = num_splits
-        self.pool = dev(x["pool"], spec.dtype)
+        self.pool = dev(x["pages"] if cache == "fp8" else x["pool"], spec.dtype)
         self.block_table = dev(x["block_table"], spec.dtype)
         self.seq_lens = dev(x["seq_lens"], spec.dtype)
         self.w_uk = dev(x["w_uk"], spec.dtype)
@@ -194,7 +225,7 @@ def oracle_decode(x: dict, batches=None, heads=None, appended_rows=None, q=None)
     for b in batches:
         L = int(x["seq_lens"][b])
         nblk = (L + bs - 1) // bs
-        sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)   # this sequence's blocks, in order
+        sub = pool_blocks(x, x["block_table"][b, :nblk])   # this sequence's blocks, in order
         if appended_rows is not None:
             for t, p in enumerate(x["positions"][b]):
                 sub[p // bs, p % bs] = appended_rows[b, t]
@@ -215,7 +246,7 @@ def oracle_query_samples(x: dict, samples):
     for b, s, h in samples:
         n = int(x["seq_lens"][b]) - spec.sq + s + 1
         nblk = (n + bs - 1) // bs
-        sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)
+        sub = pool_blocks(x, x["block_table"][b, :nblk])
         o, l = mla_oracle.decode(qn[b:b + 1, s:s + 1], qr[b:b + 1, s:s + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :],
                                  [n], x["scale"], bs, heads=[h])
         res.append((o[0, 0, h], l[0, 0, h]))

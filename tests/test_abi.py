@@ -249,3 +249,48 @@ def test_prepared_launchers_check_on_every_call():
     with pytest.raises(mla.MlaError) as err:
         append()
     assert err.value.code == -2
+
+
+def test_fp8_cache_entry_points_on_the_host():
+    """The FP8 cache type: its byte accounting, the quantise entry point's argument errors,
+    append's required workspace, and which entry points take it (every call below fails
+    validation before anything is launched)."""
+    lib = mla.raw_library()
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    f8 = mla.dims(128, 128, 64, 512, 5120, dtype="bf16_fp8")
+    page = mla.MLA_FP8_PAGE_BYTES
+    assert page == 64 * (512 + 128 + 4)
+    assert mla.mla_cache_bytes(f8, 1) == page and mla.mla_cache_bytes(f8, 64) == page
+    assert mla.mla_cache_bytes(f8, 65) == 2 * page and mla.mla_cache_bytes(f8, 0) == 0
+    assert mla.mla_cache_bytes(f8, 8192 * 64) == 8192 * 64 * 644   # 644 B per token against 1152
+
+    def quant(d, src=FAKE, dst=FAKE, nb=4):
+        return lib.mla_cache_quantize(ctypes.byref(d), src, dst, nb, None)
+    assert quant(v2) == -3                      # the destination type must be the FP8 cache
+    assert quant(f8, src=None) == -1
+    assert quant(f8, dst=None) == -1
+    assert quant(f8, nb=0) == -2
+    assert quant(f8, dst=FAKE + 4) == -4
+    assert quant(f8, src=FAKE + 8) == -4
+    assert quant(f8, nb=1 << 25) == -6
+    assert quant(mla.dims(128, 128, 64, 256, 5120, dtype="bf16_fp8")) == -8
+
+    # append: staging rows (bf16, rounded up to 256 B) + the split path's partial products
+    need = lib.mla_cache_append_workspace_bytes(ctypes.byref(f8), 2, 1)
+    assert need == 2304 + 16 * 2 * 576 * 4
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(f8), 2, 1024) == 2048 * 1152   # GEMM path: staging only
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, 2, 1, None, 0, None, None]
+    assert lib.mla_cache_append(ctypes.byref(f8), *args) == -5        # the workspace is required
+    small = list(args)
+    small[10], small[11] = FAKE, need - 1
+    assert lib.mla_cache_append(ctypes.byref(f8), *small) == -5
+
+    # decode takes the FP8 cache (same checks as bf16); prefill does not
+    assert _decode(f8, ws_bytes=1024) == -5
+    assert _decode(f8, sq=9) == -6
+    assert _decode(f8, cache=FAKE + 8) == -4
+    assert mla.mla_decode_workspace_bytes(f8, 64, 1, 256) == mla.mla_decode_workspace_bytes(v2, 64, 1, 256)
+    assert _prefill(f8) == -8
+    assert mla.mla_prefill_workspace_bytes(f8, 2, 4) == 0
+    # the layer's projections take its bf16 tensors
+    assert mla.mla_layer_workspace_bytes(f8, 1536, 64, 1) == mla.mla_layer_workspace_bytes(v2, 1536, 64, 1)
