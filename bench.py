@@ -13,6 +13,12 @@ dominant kernel (the split-KV attention) against the MI355X HBM peak, timed
 with HIP events around each of its launches on the stream it runs on.
 ``cpu_baseline`` times the fp64 oracle on the host over a bounded sample of
 the same workload.
+
+``--workload v2_b64_ctx8192_paged_append_fp8`` runs the same step with the
+cache in FP8 pages (E4M3 codes, a per-token power-of-two scale, bf16 rotary
+key: 644 B per token), quantised on the GPU from the generated bf16 cache
+before the timed region; its algorithmic bytes count 644 B per cached and
+appended token.
 """
 from __future__ import annotations
 
@@ -29,22 +35,31 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_b64_ctx8192_hbm_traffic.md")
-ATTN_SOURCES = ("mla_rank_latent_amd/csrc/attn_bf16.hip", "mla_rank_latent_amd/csrc/attn_common.h",
-                "mla_rank_latent_amd/csrc/device_util.h",
-                "mla_rank_latent_amd/csrc/mla_internal.h")
+FP8_SUFFIX = "_fp8"   # a decode workload with its cache in FP8 pages
+_COMMON_SOURCES = ("mla_rank_latent_amd/csrc/attn_common.h", "mla_rank_latent_amd/csrc/device_util.h",
+                   "mla_rank_latent_amd/csrc/mla_internal.h")
+# the counter profile of each decode workload's attention kernel, and the sources it was taken from
+TRAFFIC_PROFILES = {
+    "v2_b64_ctx8192_paged_append": ("attn_bf16_b64_ctx8192_hbm_traffic.md",
+                                    ("mla_rank_latent_amd/csrc/attn_bf16.hip",) + _COMMON_SOURCES),
+    "v2_b64_ctx8192_paged_append_fp8": ("attn_fp8_b64_ctx8192_hbm_traffic.md",
+                                        ("mla_rank_latent_amd/csrc/attn_fp8.hip",) + _COMMON_SOURCES),
+}
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter profile, or None when the profile is for
-    another workload or the attention sources changed since the counters were taken."""
+    """HBM bytes per attention launch from the committed counter profile, or None when there is none for
+    this workload or the attention sources changed since the counters were taken."""
+    if workload not in TRAFFIC_PROFILES:
+        return None
+    name, sources = TRAFFIC_PROFILES[workload]
     try:
-        text = open(TRAFFIC_PROFILE, encoding="utf-8").read()
+        text = open(os.path.join(ROOT, "profiles", name), encoding="utf-8").read()
     except OSError:
         return None
     fields = dict(re.findall(r"^- ([a-z0-9_]+): (\S+)$", text, flags=re.M))
     h = hashlib.sha256()
-    for rel in ATTN_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     if fields.get("workload") != workload or fields.get("attention_sources_sha256") != h.hexdigest():
@@ -52,21 +67,23 @@ def measured_traffic(workload: str):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def workload_bytes_flops(spec, seq_lens):
-    """Algorithmic bytes and flops of one step, with their parts."""
+def workload_bytes_flops(spec, seq_lens, fp8: bool = False):
+    """Algorithmic bytes and flops of one step, with their parts.  fp8: the cache holds, per token, d_c
+    E4M3 codes, the bf16 rotary key and one fp32 scale (644 B for DeepSeek-V2's widths)."""
     H, dn, dr, dc, d = spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model
     R = dc + dr
     e = 2 if spec.dtype == "bf16" else 4
+    row = dc + 2 * dr + 4 if fp8 else R * e                 # cache bytes per token
     tokens = int(sum(int(L) for L in seq_lens))
     B, S = spec.batch, spec.sq
-    cache = tokens * R * e                                  # every cached row read once
+    cache = tokens * row                                    # every cached row read once
     weights_dec = 2 * H * dn * dc * e                       # W^UK and W^UV
     q_bytes = B * S * H * (dn + dr) * e
     out_bytes = B * S * H * dn * e
     append_bytes = 0
     append_flops = 0
     if spec.append:
-        append_bytes = (R * d + B * S * d + B * S * R) * e   # W^DKV, W^KR, h, written rows
+        append_bytes = (R * d + B * S * d) * e + B * S * row   # W^DKV, W^KR, h, written rows
         append_flops = 2 * B * S * R * d
     # scores over [c | k^R] (576) and the latent weighted sum (512) per visible token and query row
     vis = 0
@@ -77,7 +94,8 @@ def workload_bytes_flops(spec, seq_lens):
     proj_flops = 2 * 2 * B * S * H * dn * dc                # absorption and up-projection
     total_bytes = cache + weights_dec + q_bytes + out_bytes + append_bytes
     total_flops = attn_flops + proj_flops + append_flops
-    return dict(bytes=total_bytes, flops=total_flops, cache_bytes=cache, attn_flops=attn_flops, tokens=tokens)
+    return dict(bytes=total_bytes, flops=total_flops, cache_bytes=cache, attn_flops=attn_flops, tokens=tokens,
+                row_bytes=row)
 
 
 def prefill_flops(spec, seq_lens):
@@ -399,9 +417,11 @@ def cpu_baseline_layer(x, budget_s: float, step_bytes: int):
                       f"W^O) in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
 
 
-def cpu_baseline(x, budget_s: float):
+def cpu_baseline(x, budget_s: float, fp8: bool = False):
     """Time the fp64 oracle (as it stands) on whole sequences of the workload until
-    ``budget_s`` of CPU work has been spent; scale to GB/s of the same algorithmic bytes."""
+    ``budget_s`` of CPU work has been spent; scale to GB/s of the same algorithmic bytes.
+    fp8: the oracle also quantises each sequence's blocks (and its appended row) and
+    decodes the dequantised values, as the FP8 cache stands for them."""
     import numpy as np
     from mla_rank_latent_amd import synth
     from oracle import mla_oracle
@@ -420,10 +440,15 @@ def cpu_baseline(x, budget_s: float):
         nblk = (L + bs - 1) // bs
         sub = synth.as_float(x["pool"][x["block_table"][b, :nblk]], spec.dtype)
         t0 = time.perf_counter()
+        if fp8:
+            codes, scales, rope = mla_oracle.quantize_rows(sub, spec.d_latent)
+            sub = mla_oracle.dequantize_rows(codes, scales, rope)
         if spec.append:
             rows = mla_oracle.cache_rows(synth.as_float(x["h"][b:b + 1], spec.dtype),
                                          synth.as_float(x["w_dkv"], spec.dtype), synth.as_float(x["w_kr"], spec.dtype),
                                          x["positions"][b:b + 1], spec.rope_base, spec.dtype)
+            if fp8:
+                rows = mla_oracle.dequantize_rows(*mla_oracle.quantize_rows(rows, spec.d_latent))
             for t, p in enumerate(x["positions"][b]):
                 sub[p // bs, p % bs] = rows[0, t]
         mla_oracle.decode(qn[b:b + 1], qr[b:b + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :], [L], x["scale"], bs)
@@ -432,11 +457,12 @@ def cpu_baseline(x, budget_s: float):
         if spent >= budget_s:
             break
     # the sampled sequences are `done` of `batch`; weights are counted in proportion
-    wb = workload_bytes_flops(spec, x["seq_lens"])["bytes"]
+    wb = workload_bytes_flops(spec, x["seq_lens"], fp8)["bytes"]
     value = wb * done / spec.batch / spent / 1e9
+    what = ", FP8 quantise/dequantise included" if fp8 else ""
     return {"value": round(value, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {spec.batch} sequences (all {spec.n_heads} heads, full context, append included) "
-                      f"in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
+            "sample": f"{done} of {spec.batch} sequences (all {spec.n_heads} heads, full context, append included"
+                      f"{what}) in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
 
 
 def main() -> int:
@@ -471,7 +497,12 @@ def main() -> int:
         return 0
 
     prefill, layer = synth.prefill_presets(), synth.layer_presets()
-    spec = {**synth.presets(), **prefill, **layer}[args.workload]
+    fp8 = args.workload.endswith(FP8_SUFFIX)
+    base = args.workload[:-len(FP8_SUFFIX)] if fp8 else args.workload
+    spec = {**synth.presets(), **prefill, **layer}[base]
+    if fp8 and base not in synth.presets():
+        print(f"bench.py: the FP8 cache applies to the decode workloads, not {base}", file=sys.stderr)
+        return 2
     print(f"[bench] generating {spec.name} (seed {spec.seed})", file=sys.stderr, flush=True)
     x = synth.make_inputs(spec)
     if args.workload in prefill:
@@ -485,9 +516,15 @@ def main() -> int:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    d = mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size, spec.dtype,
-                 spec.rope_base)
+    d = mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size,
+                 "bf16_fp8" if fp8 else spec.dtype, spec.rope_base)
     pool, bt, lens = dev(x["pool"]), dev(x["block_table"]), dev(x["seq_lens"])
+    if fp8:
+        # the cache in FP8 pages, quantised on the GPU from the generated bf16 cache
+        pages = torch.empty(pool.shape[0], mla.MLA_FP8_PAGE_BYTES, dtype=torch.uint8, device="cuda")
+        mla.mla_cache_quantize(d, pool, pages)
+        torch.cuda.synchronize()
+        pool = pages
     w_uk, w_uv = dev(x["w_uk"]), dev(x["w_uv"])
     qn, qr = dev(x["q_nope"]), dev(x["q_rope"])
     has_append = spec.append
@@ -547,7 +584,7 @@ def main() -> int:
           f"attention {ms_attn * 1e3:.1f} us; host issue {enqueued / args.steps * 1e6:.1f} us/step", file=sys.stderr,
           flush=True)
 
-    wl = workload_bytes_flops(spec, x["seq_lens"])
+    wl = workload_bytes_flops(spec, x["seq_lens"], fp8)
     step_s = ms_step * 1e-3
     gbs = wl["bytes"] / step_s / 1e9
     tflops = wl["flops"] / step_s / 1e12
@@ -568,11 +605,12 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic (seeded N(0,1) cache/queries/hidden states, N(0,1/fan_in) weights)",
-        "config": {"workload": spec.name, "batch": spec.batch, "context": int(max(x["seq_lens"])),
+        "config": {"workload": args.workload, "batch": spec.batch, "context": int(max(x["seq_lens"])),
                    "query_tokens": spec.sq, "heads": spec.n_heads, "d_latent": spec.d_latent,
                    "d_rope": spec.d_rope, "d_nope": spec.d_nope, "d_model": spec.d_model,
                    "block_size": spec.block_size, "paged": spec.paged, "append": spec.append,
-                   "num_splits": args.num_splits or "auto"},
+                   "cache": "fp8_e4m3 (per-token power-of-two scale, bf16 k^R)" if fp8 else spec.dtype,
+                   "cache_bytes_per_token": wl["row_bytes"], "num_splits": args.num_splits or "auto"},
         "tflops": round(tflops, 2),
         "tokens_per_s": round(tok_s, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -580,8 +618,8 @@ def main() -> int:
         "step_bytes": wl["bytes"],
         "step_flops": wl["flops"],
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(spec.name),
-                     "kernel": "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                     "kernel": "attn_fp8_kernel" if fp8 else "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
                      "bytes_per_launch": wl["cache_bytes"],
                      "mfma_tflops": round(attn_tflops, 2),
                      "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -589,7 +627,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (oracle, ~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget, fp8)
     print(json.dumps(res), flush=True)
     return 0
 
