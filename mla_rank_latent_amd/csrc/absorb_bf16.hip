@@ -3,8 +3,11 @@
 // "DeepSeek-V2: Multi-Head Latent Attention (MLA) 原理与工程实现" §2.2: the query-key
 // product through the up-projection, q^C . (W^UK_i c), equals (W^UK_i^T q^C) . c,
 // so each head's query is moved into the d_c-wide latent space once per step:
-//   q_lat[m, i, 0:512]   = W^UK_i^T q^C[m, i]     (W^UK_i = rows 128 i .. 128 i + 127 of W^UK)
-//   q_lat[m, i, 512:576] = q^R[m, i]               (already rotated, §3.2)
+//   q_lat[m, i, 0:512]   = s2 W^UK_i^T q^C[m, i]     (W^UK_i = rows 128 i .. 128 i + 127 of W^UK)
+//   q_lat[m, i, 512:576] = s2 q^R[m, i]               (already rotated, §3.2)
+// with s2 the power of two nearest to softmax scale * log2(e): the scaling is
+// exact (q^R stays the caller's bf16 values up to the exponent) and the
+// attention kernels apply the remaining factor, within [0.71, 1.42], in fp32.
 // One workgroup per (head, 128 latent columns): the 128 x 128 slice of W^UK_i
 // is staged in LDS once and used for every query row m, as a batched GEMM
 // [M x 128] . [128 x 128] on MFMA 32x32x16.  The contraction runs along the
@@ -31,8 +34,8 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           const int32_t* __restrict__ seq_lens, int max_blocks,
-                                                          int batch, int sq, int n_heads, uint8_t* __restrict__ ws,
-                                                          WsLayout Lw, int32_t* status) {
+                                                          int batch, int sq, int n_heads, float qscale,
+                                                          uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
   // block 0 builds the split plan: dispatched first, it overlaps the rest of the grid
   if (blockIdx.x == 0) {
     plan_build(seq_lens, batch, sq, max_blocks, kBlk, Lw.align, Lw.W, ws, Lw, status);
@@ -94,12 +97,16 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
     }
   };
   stage_q(0);
-  // the rotary half of the latent query is a copy
+  // the rotary half of the latent query: q^R times a power of two (exact)
   if (cb == 0) {
     for (int i = tid; i < M * (kRope / 8); i += 256) {
       int m = i / (kRope / 8), j = i % (kRope / 8);
-      *(u32x4*)(q_lat + ((size_t)m * n_heads + h) * kRow + kLat + 8 * j) =
-          *(const u32x4*)(q_rope + ((size_t)m * n_heads + h) * kRope + 8 * j);
+      const u32x4 v = *(const u32x4*)(q_rope + ((size_t)m * n_heads + h) * kRope + 8 * j);
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf2(bf2f((uint16_t)(v[e] & 0xffffu)) * qscale, bf2f((uint16_t)(v[e] >> 16)) * qscale);
+      *(u32x4*)(q_lat + ((size_t)m * n_heads + h) * kRow + kLat + 8 * j) = o;
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int mm = mb * 64 + 32 * half + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (mm < M) q_lat[((size_t)mm * n_heads + h) * kRow + col] = f2bf(acc[i]);
+        if (mm < M) q_lat[((size_t)mm * n_heads + h) * kRow + col] = f2bf(acc[i] * qscale);
       }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // next block landed (and this block's stores issued)
@@ -158,11 +165,11 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
 }
 
 hipError_t launch_absorb_bf16(const WsLayout& L, const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
-                              const int32_t* seq_lens, int max_blocks, int batch, int sq, int n_heads, uint8_t* ws,
-                              int32_t* status, hipStream_t st) {
+                              const int32_t* seq_lens, int max_blocks, int batch, int sq, int n_heads, float qscale,
+                              uint8_t* ws, int32_t* status, hipStream_t st) {
   dim3 grid(n_heads * 4 + 1);
   hipLaunchKernelGGL(absorb_bf16_kernel, grid, dim3(256), 0, st, q_nope, q_rope, w_uk, seq_lens, max_blocks, batch,
-                     sq, n_heads, ws, L, status);
+                     sq, n_heads, qscale, ws, L, status);
   return hipGetLastError();
 }
 

@@ -113,6 +113,19 @@ bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L
   return true;
 }
 
+void split_softmax_scale(float softmax_scale, float* qscale, float* zscale) {
+  const double s = (double)softmax_scale * 1.4426950408889634;   // log2(e): exponentials in base 2
+  if (s == 0.0) {   // every logit is zero
+    *qscale = 0.0f;
+    *zscale = 1.0f;
+    return;
+  }
+  // the exponent is clamped so that qscale stays a normal float for any finite scale
+  const double p2 = std::exp2(std::fmin(std::fmax(std::nearbyint(std::log2(std::fabs(s))), -100.0), 100.0));
+  *qscale = (float)(s < 0.0 ? -p2 : p2);
+  *zscale = (float)(std::fabs(s) / p2);
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -346,14 +359,16 @@ int decode_phases(int phases, const mla_dims* dims, const void* q_nope, const vo
   uint8_t* ws = (uint8_t*)workspace;
   hipError_t e = hipSuccess;
   if (is_bf(dims)) {
+    float qscale, zscale;
+    split_softmax_scale(softmax_scale, &qscale, &zscale);
     if (phases & kPhasePrepare)
       e = launch_absorb_bf16(L, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, seq_lens,
-                             max_blocks, batch, sq, dims->n_heads, ws, status, st);
+                             max_blocks, batch, sq, dims->n_heads, qscale, ws, status, st);
     if (e == hipSuccess && (phases & kPhaseAttend))
       e = is_fp8(dims) ? launch_attn_fp8(L, (const uint8_t*)cache, num_blocks, block_table, max_blocks, seq_lens,
-                                         batch, sq, dims->n_heads, softmax_scale, ws, status, st)
+                                         batch, sq, dims->n_heads, zscale, ws, status, st)
                        : launch_attn_bf16(L, (const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens,
-                                          batch, sq, dims->n_heads, softmax_scale, ws, status, st);
+                                          batch, sq, dims->n_heads, zscale, ws, status, st);
     if (e == hipSuccess && (phases & kPhaseFinish))
       e = launch_merge_upv_bf16(L, (const uint16_t*)w_uv, batch, sq, dims->n_heads, ws, (uint16_t*)out, lse, st);
   } else {

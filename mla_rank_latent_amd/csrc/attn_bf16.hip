@@ -2,27 +2,36 @@
 //
 // What it computes ("DeepSeek-V2: Multi-Head Latent Attention (MLA) 原理与工程实现",
 // §2.2 matrix absorption and §3.2 decoupled RoPE): for every query row
-// (head i, query token s) with absorbed query q_lat = [W^UK_i^T q^C ‖ q^R],
-// the logits z_j = scale * q_lat . [c_j ‖ k^R_j] over one range of cached
-// tokens, softmax weights against a per-row reference maximum, and the
-// latent weighted sum sum_j p_j c_j.  Every range leaves a partial state
-// (latent sum, reference maximum, weight sum) that the merge kernel combines.
+// (head i, query token s) with absorbed query q_lat = [W^UK_i^T q^C ‖ q^R]
+// (pre-scaled by a power of two s2, which rounds nothing), the logits in log2
+// units z_j = zscale * q_lat . [c_j ‖ k^R_j], zscale * s2 = softmax scale *
+// log2(e), over one range of cached tokens,
+// softmax weights against a per-row reference maximum, and the latent
+// weighted sum sum_j p_j c_j.  Every range leaves a partial state (latent
+// sum, reference maximum, weight sum) that the merge kernel combines.
 //
 // Mapping onto the chip.  All heads share one latent stream, so a workgroup
 // takes 128 query rows (all 128 heads at Sq = 1) against the same cache
 // tiles, and both contractions are dense GEMMs on MFMA 32x32x16 (the shape
-// one wave can issue at the matrix core's full rate):
-//   S^T[32 tok x 32 rows]  = T[32 tok x 576] . Q^T[576 x 32 rows]     (36 MFMAs)
-//   O^T[512 x 32 rows]    += C^T[512 x 32 tok] . P^T[32 tok x 32 rows] (32 MFMAs)
-// per wave and 32-token stage.  Four waves of 32 rows, one per SIMD: a wave
-// keeps its Q (144 VGPRs) and its O accumulator (256 AGPRs) in registers for
-// the whole range, and every 16-byte LDS operand read feeds a full 32-row
-// MFMA.  The cache tile is read from HBM once per workgroup.
+// one wave can issue at the matrix core's full rate).  Four waves, one per
+// SIMD; per wave and 32-token stage:
+//   scores  S^T[32 tok x 32 rows] = T[32 tok x 576] . Q^T[576 x 32 rows] for the
+//           wave's own 32 rows (36 MFMAs, one accumulation chain: dependent
+//           MFMAs of one opcode issue back to back);
+//   latent  O^T[128 feat x 128 rows] += C^T[128 feat x 32 tok] . P^T[32 tok x 128 rows]
+//           for the wave's own quarter of the 512 latent features and all 128
+//           rows (32 MFMAs).
+// A wave keeps its Q (144 VGPRs) and its O quarter (256 AGPRs) in registers
+// for the whole range.  The softmax weights P of a stage go through LDS
+// (8 KB, double-buffered), so every tile operand a wave reads for the latent
+// product feeds four MFMAs (one per row block) and the transposing tile reads
+// drop to a quarter.  The cache tile is read from HBM once per workgroup.
 //  - Software pipeline: iteration it scores stage it, then runs the latent
-//    product of stage it - 1 while the vector units compute stage it's
-//    softmax weights.  The score accumulators live in VGPRs (the score MFMAs
-//    are issued as asm in their VGPR form), the latent accumulators in AGPRs,
-//    so no accumulator is ever moved between the two register files.
+//    product of stage it - 1 with stage it's softmax interleaved between its
+//    MFMAs step by step (the exponentials spread over the whole product).
+//    The score accumulators live in VGPRs (the score MFMAs are issued as asm
+//    in their VGPR form), the latent accumulators in AGPRs, so no accumulator
+//    is ever moved between the two register files.
 //  - Tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging)
 //    into a 4-slot ring of 36 KB stages: one being multiplied, one being
 //    scored, two in flight.  A wave's copies are issued between its score
@@ -32,16 +41,18 @@
 //    chunks).  Measured with the LDS bank-conflict counter on gfx950, this
 //    makes both the score operand reads (ds_read_b128: 32 rows x 2 chunks)
 //    and the transposing PV operand reads (ds_read_b64_tr_b16: 4 rows x 4
-//    feature quads per 16 lanes) conflict free at 256 B/clk.
+//    feature quads per 16 lanes) conflict free.
 //  - The PV product needs the tile with tokens along K; the LDS transpose
 //    read delivers that from the token-major tile, in the token order in
-//    which the S result already sits in registers, so P never leaves them.
+//    which the S result sits in registers, which is also the order in which
+//    P is stored and read back as the MFMA's B operand.
 //  - Scores against a fixed per-row reference (the first stage's maximum):
 //    p = 2^(z - ref) <= 2^16 unless a later score beats the reference by
 //    more than 16, in which case the range is re-run against the largest
 //    score seen (exact; for real logit spreads it never happens).  O is never
 //    rescaled in registers, so its accumulators are written only by MFMAs
-//    and stay in AGPRs.
+//    and stay in AGPRs.  The weight sum adds the bf16-rounded weights (a
+//    packed dot product with ones), the same values the latent product uses.
 #include "attn_common.h"
 
 namespace mla {
@@ -56,8 +67,9 @@ constexpr int kRowsPerWave = 32;
 static_assert(kWaves * kRowsPerWave == kRowsWG, "rows per workgroup");
 constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;   // 9 copies of 1 KB per wave and stage
 constexpr int kPfS = 4;   // score operands read ahead
-constexpr int kPfO = 5;   // PV operands read ahead
+constexpr int kPBytes = kRowsWG * kSubTok * 2;   // one stage's weights for all rows: 8 KB
 
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};   // weight sum as a packed dot product
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
 
 }  // namespace
@@ -65,15 +77,14 @@ __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ cache, int num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ seq_lens, int batch, int sq, int n_heads, int hg, int W, int P,
-    float scale_log2, uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
-  // the ring, then 1 KB that absorbs the copies of iterations with no stage left to fetch
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + 1024];
+    float zscale, uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
+  // the ring, then two 8 KB slots of softmax weights (bf16) shared by the waves
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + 2 * kPBytes];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
-  __shared__ int s_retry;
-  if (threadIdx.x == 0) s_retry = 0;
+  MLA_LDS uint8_t* pbuf = lds + kStages * kStageBytes;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;     // row within the wave's 32 (MFMA column)
   const int hh = lane >> 5;    // lane half
@@ -180,7 +191,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   // into the spare kilobyte.  Every iteration issues the same number of copies,
   // so one fixed wait count finds each stage landed.
   const uint64_t idle_base = uniform_addr(cache);
-  const uint32_t idle_dst = (uint32_t)(uintptr_t)(lds + kStages * kStageBytes);
 
   int seg_i = wgseg[w];
   u32x4 qreg[36];
@@ -235,15 +245,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       if (k < nsub) {
         issue_stage(k, stage_base(lookup_block(b, a + k * kSubTok), a + k * kSubTok), tlast_of(k));
       } else {
+        const uint32_t idle_dst = (uint32_t)(uintptr_t)(lds + k * kStageBytes + wave * 1024);
 #pragma unroll
-        for (int c = 0; c < kLoadsPerWave; ++c) copy16_to_lds(idle_base, ld_off(c), idle_dst);
+        for (int c = 0; c < kLoadsPerWave; ++c) copy16_to_lds(idle_base, ld_off(c), __builtin_amdgcn_readfirstlane(idle_dst));
       }
     }
+    // the weights of the (empty) stage before the first: zero
+    *(MLA_LDS u32x4*)(pbuf + kPBytes + wave * 2048 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    *(MLA_LDS u32x4*)(pbuf + kPBytes + wave * 2048 + 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     // block ids are looked up one stage ahead of their copies, so that the
     // scalar load's latency is hidden behind a whole stage of work
     int blk_next = 2 < nsub ? lookup_block(b, a + 2 * kSubTok) : 0;
-    // softmax weights of the previous stage (bf16 pairs), consumed one iteration later
-    uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 
     // Iteration it scores stage it and, interleaved with that stage's softmax,
     // runs the latent product of stage it - 1, so the softmax's vector work
@@ -253,21 +265,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       // (issued by the previous iteration) remains in flight.
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave));
       __syncthreads();   // stage it visible to all waves; stage it - 2 fully consumed
-      // The copies of stage it + 2 ride along the score MFMAs below.  A ragged
-      // stage (a sequence's last) goes out here in full, with its rows clamped.
+      // The copies of stage it + 2 ride along the score MFMAs below.  A ragged stage (a
+      // sequence's last) re-reads its last valid row in place of the rows past it.  With no
+      // stage left to fetch, the copies land in the slot stage it + 2 would use: no later
+      // iteration of this range reads it.
       uint64_t nbase = idle_base;
-      uint32_t ndst = idle_dst, nstride = 0;
+      uint32_t ndst = (uint32_t)(uintptr_t)(lds + ((it + 2) & 3) * kStageBytes + wave * 1024), nstride = 0;
+      int ntl = kSubTok - 1;   // last valid row of the stage fetched
       if (it + 2 < nsub) {
-        const int tok = a + (it + 2) * kSubTok;
-        const int tl = tlast_of(it + 2);
-        const uint64_t base = stage_base(blk_next, tok);
-        if (tl == kSubTok - 1) {
-          nbase = base;
-          ndst = (uint32_t)(uintptr_t)(lds + ((it + 2) & 3) * kStageBytes + wave * 1024);
-          nstride = kWaves * 1024;
-        } else {
-          issue_stage((it + 2) & 3, base, tl);
-        }
+        nbase = stage_base(blk_next, a + (it + 2) * kSubTok);
+        nstride = kWaves * 1024;
+        ntl = tlast_of(it + 2);
       }
       if (it + 3 < nsub) blk_next = lookup_block(b, a + (it + 3) * kSubTok);
       const bool valid = it < nsub;
@@ -277,9 +285,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       const MLA_LDS uint8_t* sto = lds + ((it > 0 ? it - 1 : 0) & 3) * kStageBytes;
       const int tok0 = a + it * kSubTok;
 
+      // latent-product operands (stage it - 1), the first of them read during the score MFMAs
+      const MLA_LDS uint8_t* pp = pbuf + ((it + 1) & 1) * kPBytes + lane * 16;
+      // A operand a = 4 hs + fb: feature block 4 wave + fb, token half hs; its two reads
+      // take tokens 16 hs + 4 hh + e (r = 0) and 16 hs + 8 + 4 hh + e (r = 1)
+      auto rd = [&](int a) {
+        const int hs = a >> 2, FB = 4 * wave + (a & 3);
+        const int o0 = (o_off[FB & 1] ^ (16 * (4 * hs))) + (FB >> 1) * 128 + (16 * hs) * (kRow * 2);
+        const int o1 = (o_off[FB & 1] ^ (16 * (4 * hs + 2))) + (FB >> 1) * 128 + (16 * hs + 8) * (kRow * 2);
+        const u32x2 lo2 = lds_read_tr16(sto + o0);
+        const u32x2 hi2 = lds_read_tr16(sto + o1);
+        return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      };
+      u32x4 pb[2][4], av[8];
+
       // ---- S^T = T . Q^T (32 tokens x 32 rows), 36 k-steps of 16 features
-      // two independent accumulation chains (even / odd k-steps) keep the matrix core busy
-      f32x16 acc_s, acc_s1;
+      // one accumulation chain: dependent MFMAs of one opcode issue back to back
+      f32x16 acc_s;
       {
         u32x4 tv[kPfS];
 #pragma unroll
@@ -288,91 +310,99 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
         for (int ks = 0; ks < 36; ++ks) {
           const u32x4 t = tv[ks % kPfS];
           if (ks + kPfS < 36) tv[ks % kPfS] = lds_read16(st + s_off[(ks + kPfS) & 3] + ((ks + kPfS) >> 2) * 128);
-          if (ks < 2) mfma_s_first(ks & 1 ? acc_s1 : acc_s, t, qreg[ks]);
-          else mfma_s(ks & 1 ? acc_s1 : acc_s, t, qreg[ks]);
-          if ((ks & 3) == 2)
-            copy16_to_lds(nbase, ld_off(ks >> 2), __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
+          if (ks == 0) mfma_s_first(acc_s, t, qreg[ks]);
+          else mfma_s(acc_s, t, qreg[ks]);
+          if ((ks & 3) == 2) {
+            uint32_t o = ld_off(ks >> 2);
+            if (ntl < kSubTok - 1) {   // wave-uniform: only a sequence's last, ragged stage
+              const int r = (int)(o / (kRow * 2));
+              if (r > ntl) o -= (uint32_t)((r - ntl) * (kRow * 2));
+            }
+            copy16_to_lds(nbase, o, __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
+          }
+          if (ks == 32) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) pb[0][rb] = lds_read16(pp + rb * 2048);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        settle_s(acc_s, acc_s1);
+        settle_s(acc_s);
+      }
+      if (!valid || tok0 + kSubTok - 1 > L - sq) {   // past some row's last visible token, or no stage
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tok0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool off = !valid || tok > lim;
+          acc_s[r] = off ? kNegInf : acc_s[r];
+        }
       }
 
-      // ---- softmax weights of stage it against the row reference (log2 units),
-      // interleaved below with the latent product of stage it - 1.  Lane holds
-      // row n and tokens 8 (r / 4) + 4 hh + r % 4, r = 0..15.
+      // ---- softmax weights of stage it against the row reference (log2 units; the lane
+      // holds row n and tokens 8 (r / 4) + 4 hh + r % 4, r = 0..15), interleaved step by
+      // step with the latent product of stage it - 1:
+      //   O^T += C^T . P^T over this wave's 128 features (4 blocks of 32) x all 128 rows
+      //   (4 row blocks) x 2 token halves, 32 MFMAs.  P comes from LDS, written there by
+      //   the wave that owns each row block.
       uint32_t pk[8];
       {
+        av[0] = rd(0);
+        av[1] = rd(1);
         float z[16];
+        float mx = 0.0f, msafe = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = (acc_s[r] + acc_s1[r]) * scale_log2;
-        if (!valid || tok0 + kSubTok - 1 > L - sq) {   // past some row's last visible token, or no stage
+        for (int j = 0; j < 32; ++j) {
+          const int hs = j >> 4, fb = (j >> 2) & 3, rb = j & 3, ai = 4 * hs + fb;
+          acc_o[4 * fb + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(av[ai]), as_bf8(pb[hs][rb]),
+                                                                       acc_o[4 * fb + rb], 0, 0, 0);
+          if (rb == 0 && ai + 2 < 8) av[ai + 2] = rd(ai + 2);
+          if (j == 8) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tok = tok0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            z[r] = (!valid || tok > lim) ? kNegInf : z[r];
+            for (int r2 = 0; r2 < 4; ++r2) pb[1][r2] = lds_read16(pp + r2 * 2048 + 1024);
           }
-        }
-        float mx = z[0];
+          if (j < 4) {
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, z[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        m_run = fmaxf(m_run, mx);
-        m_ref = m_ref == kNegInf ? mx : m_ref;   // a row's reference: its first finite stage maximum
-        bad = bad || (mx > m_ref + kLazyTau);
-        const float msafe = m_ref == kNegInf ? 0.0f : m_ref;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(z[r] - msafe);
-          const float p1 = __builtin_amdgcn_exp2f(z[r + 1] - msafe);
-          l_sum += p0 + p1;
-          pk[r >> 1] = pack_bf2(p0, p1);
-        }
-      }
-
-      // ---- O^T += C^T . P^T for stage it - 1 (512 features x 32 rows): 16 feature
-      // blocks x 2 token halves
-      {
-        const u32x4 pb0 = {pk_prev[0], pk_prev[1], pk_prev[2], pk_prev[3]};
-        const u32x4 pb1 = {pk_prev[4], pk_prev[5], pk_prev[6], pk_prev[7]};
-        // operand j: feature block fb = j & 15, token half hs = j >> 4; its two reads take
-        // tokens 16 hs + 4 hh + e (r = 0) and 16 hs + 8 + 4 hh + e (r = 1)
-        auto rd = [&](int j) {
-          const int fb = j & 15, hs = j >> 4;
-          const int o0 = (o_off[fb & 1] ^ (16 * (4 * hs))) + (fb >> 1) * 128 + (16 * hs) * (kRow * 2);
-          const int o1 = (o_off[fb & 1] ^ (16 * (4 * hs + 2))) + (fb >> 1) * 128 + (16 * hs + 8) * (kRow * 2);
-          const u32x2 lo2 = lds_read_tr16(sto + o0);
-          const u32x2 hi2 = lds_read_tr16(sto + o1);
-          return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-        };
-        u32x4 av[kPfO];
-#pragma unroll
-        for (int k = 0; k < kPfO; ++k) av[k] = rd(k);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const u32x4 op = av[j % kPfO];
-          if (j + kPfO < 32) av[j % kPfO] = rd(j + kPfO);
-          acc_o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(op), as_bf8(j < 16 ? pb0 : pb1),
-                                                                  acc_o[j & 15], 0, 0, 0);
-        }
-        // reads kPfO operands ahead; between consecutive MFMAs, a share of the softmax's vector work
-#pragma unroll
-        for (int k = 0; k < kPfO; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (j + kPfO < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int r = 4 * j; r < 4 * j + 4; ++r) z[r] = acc_s[r];
+          } else if (j == 4) {
+            mx = __builtin_fmaxf(__builtin_fmaxf(z[0], __builtin_fmaxf(z[1], z[2])),
+                                 __builtin_fmaxf(__builtin_fmaxf(z[3], __builtin_fmaxf(z[4], z[5])), __builtin_fmaxf(z[6], z[7])));
+          } else if (j == 5) {
+            mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11])),
+                                 fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]))));
+          } else if (j == 6) {
+            // the other lane half holds the same row's other 16 tokens
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * zscale;   // zscale > 0
+            m_run = fmaxf(m_run, mx);
+            m_ref = m_ref == kNegInf ? mx : m_ref;   // a row's reference: its first finite stage maximum
+            bad = bad || (mx > m_ref + kLazyTau);
+            msafe = m_ref == kNegInf ? 0.0f : m_ref;
+          } else if (j < 29 && (j - 7) % 3 == 0) {
+            const int r = 2 * ((j - 7) / 3);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[r], zscale, -msafe));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[r + 1], zscale, -msafe));
+            pk[r >> 1] = pack_bf2(p0, p1);
+            l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r >> 1]), kOnes2, l_sum, false);
+          } else if (j == 29) {
+            // this stage's weights, for every wave's latent product in the next iteration
+            *(MLA_LDS u32x4*)(pbuf + (it & 1) * kPBytes + wave * 2048 + lane * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            *(MLA_LDS u32x4*)(pbuf + (it & 1) * kPBytes + wave * 2048 + 1024 + lane * 16) =
+                u32x4{pk[4], pk[5], pk[6], pk[7]};
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) pk_prev[k] = pk[k];
     }
-    if (__builtin_amdgcn_ballot_w64(bad) != 0ull && lane == 0) s_retry = 1;
-    __syncthreads();   // ring free for the next range; every wave's flag visible
-    const bool retry = s_retry != 0;
-    __syncthreads();   // every wave has read the flag
+    const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0ull;
+    __syncthreads();   // ring and weight slots free
+    MLA_LDS int* flags = (MLA_LDS int*)pbuf;
+    if (lane == 0) flags[wave] = wbad ? 1 : 0;
+    __syncthreads();   // every wave's flag visible
+    const bool retry = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+    __syncthreads();   // every wave has read the flags
     if (retry) {
       // a score beat the reference by more than 2^tau: run this range again
       // against the largest score seen (rare; exact either way)
-      if (tid == 0) s_retry = 0;
       m_again = m_run;
       again = true;
       continue;
@@ -381,13 +411,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
 
     // ---- partial state: un-normalised latent sum, reference max and weight sum
     const float l_tot = l_sum + __shfl_xor(l_sum, 32);
-    float* op = part_o + ((size_t)piece * kRowsWG + row) * kLat + 4 * hh;
 #pragma unroll
-    for (int fb = 0; fb < 16; ++fb) {
+    for (int rb = 0; rb < 4; ++rb) {
+      float* op = part_o + ((size_t)piece * kRowsWG + 32 * rb + n) * kLat + 128 * wave + 4 * hh;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 v = {acc_o[fb][4 * rr], acc_o[fb][4 * rr + 1], acc_o[fb][4 * rr + 2], acc_o[fb][4 * rr + 3]};
-        *(f32x4*)(op + fb * 32 + 8 * rr) = v;
+      for (int fb = 0; fb < 4; ++fb) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x16& A = acc_o[4 * fb + rb];
+          const f32x4 v = {A[4 * rr], A[4 * rr + 1], A[4 * rr + 2], A[4 * rr + 3]};
+          *(f32x4*)(op + fb * 32 + 8 * rr) = v;
+        }
       }
     }
     if (hh == 0) part_ml[(size_t)piece * kRowsWG + row] = make_float2(m_ref, l_tot);
@@ -395,14 +429,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
 }
 
 hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_blocks, const int32_t* block_table,
-                            int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float scale,
+                            int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float zscale,
                             uint8_t* ws, int32_t* status, hipStream_t st) {
   // grid: W ranges x G head groups, ordered so the groups of a range share an XCD
   const int wpad = (L.W + 7) / 8 * 8;
   dim3 grid(wpad * L.G);
-  const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(kWaves * 64), 0, st, cache, num_blocks, block_table, max_blocks,
-                     seq_lens, batch, sq, n_heads, L.hg, L.W, L.P, scale_log2, ws, L, status);
+                     seq_lens, batch, sq, n_heads, L.hg, L.W, L.P, zscale, ws, L, status);
   return hipGetLastError();
 }
 

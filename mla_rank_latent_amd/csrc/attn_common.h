@@ -32,6 +32,7 @@ __device__ __forceinline__ void mfma_s(f32x16& acc, u32x4 a, u32x4 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 // 24 wait states: more than an 8- or 16-pass MFMA's result needs before a vector read
+__device__ __forceinline__ void settle_s(f32x16& a0) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0)); }
 __device__ __forceinline__ void settle_s(f32x16& a0, f32x16& a1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
 }

@@ -2,8 +2,10 @@
 //
 // Same computation as the bf16-cache kernel ("DeepSeek-V2: Multi-Head Latent
 // Attention (MLA) 原理与工程实现", §2.2 matrix absorption and §3.2 decoupled
-// RoPE): for every query row with absorbed query q_lat = [W^UK_i^T q^C ‖ q^R],
-// logits z_j = scale * q_lat . [c_j ‖ k^R_j] over one range of cached tokens,
+// RoPE): for every query row with absorbed query q_lat = [W^UK_i^T q^C ‖ q^R]
+// (pre-scaled by a power of two s2), logits in log2 units
+// z_j = zscale * q_lat . [c_j ‖ k^R_j], zscale * s2 = softmax scale * log2(e),
+// over one range of cached tokens,
 // softmax weights against a per-row reference maximum, and the latent weighted
 // sum sum_j p_j c_j, left as a partial state for the merge kernel.  Here the
 // cache stores c_j = s_j * v(code_j) (E4M3 codes, one power-of-two scale per
@@ -93,7 +95,7 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const MLA_LDS uint8_t* p) {
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ pages, int num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ seq_lens, int batch, int sq, int n_heads, int hg, int W, int P,
-    float scale_log2, uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
+    float zscale, uint8_t* __restrict__ ws, WsLayout Lw, int32_t* status) {
   // the ring, 1 KB that absorbs the copies that fetch nothing needed, and the rows' q^R
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kQLds];
   MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
       {
         float z[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = (acc_s[r] + acc_s1[r]) * scale_log2;
+        for (int r = 0; r < 16; ++r) z[r] = (acc_s[r] + acc_s1[r]) * zscale;
         float sc[16];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
@@ -460,14 +462,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
 }
 
 hipError_t launch_attn_fp8(const WsLayout& L, const uint8_t* pages, int num_blocks, const int32_t* block_table,
-                           int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float scale,
+                           int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float zscale,
                            uint8_t* ws, int32_t* status, hipStream_t st) {
   // grid: W ranges x G head groups, ordered so the groups of a range share an XCD
   const int wpad = (L.W + 7) / 8 * 8;
   dim3 grid(wpad * L.G);
-  const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attn_fp8_kernel, grid, dim3(kWaves * 64), 0, st, pages, num_blocks, block_table, max_blocks,
-                     seq_lens, batch, sq, n_heads, L.hg, L.W, L.P, scale_log2, ws, L, status);
+                     seq_lens, batch, sq, n_heads, L.hg, L.W, L.P, zscale, ws, L, status);
   return hipGetLastError();
 }
 

@@ -81,15 +81,19 @@ hipError_t launch_append_f32(const mla_dims* d, const float* h, const float* w_d
                              int32_t* status, hipStream_t st);
 hipError_t launch_qproj(const mla_dims* d, const void* h, const void* w_q, const void* w_qr,
                         const int32_t* positions, void* q_nope, void* q_rope, int tokens, hipStream_t st);
+// Softmax scale split: softmax scale * log2(e) = qscale * zscale with qscale a power of two
+// (applied exactly to the absorbed query) and zscale in [0.71, 1.42] (applied to the logits).
+void split_softmax_scale(float softmax_scale, float* qscale, float* zscale);
+// absorb: q_lat = qscale * [W^UK_i^T q^C | q^R]
 hipError_t launch_absorb_bf16(const WsLayout& L, const uint16_t* q_nope, const uint16_t* q_rope,
                               const uint16_t* w_uk, const int32_t* seq_lens, int max_blocks, int batch,
-                              int sq, int n_heads, uint8_t* ws, int32_t* status, hipStream_t st);
+                              int sq, int n_heads, float qscale, uint8_t* ws, int32_t* status, hipStream_t st);
 hipError_t launch_attn_bf16(const WsLayout& L, const uint16_t* cache, int num_blocks,
                             const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
-                            int batch, int sq, int n_heads, float scale, uint8_t* ws, int32_t* status,
+                            int batch, int sq, int n_heads, float zscale, uint8_t* ws, int32_t* status,
                             hipStream_t st);
 hipError_t launch_attn_fp8(const WsLayout& L, const uint8_t* pages, int num_blocks, const int32_t* block_table,
-                           int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float scale,
+                           int max_blocks, const int32_t* seq_lens, int batch, int sq, int n_heads, float zscale,
                            uint8_t* ws, int32_t* status, hipStream_t st);
 // FP8 cache rows: quantise bf16 rows [n_rows][576] into pages.  positions == null: row r is
 // slot r % 64 of page r / 64 (a whole pool); otherwise token r goes to its position's slot
