@@ -141,20 +141,24 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   // Stage copy plan: copy q (0..35) of a stage moves stage bytes [1024 q, 1024 q + 1024);
   // wave w issues copies w, w + 4, ... .  Lane l's 16 B land at stage chunk 64 q + l:
   // token (64 q + l) / 72, physical chunk (64 q + l) % 72, holding logical chunk
-  // (physical ^ swz(token)) of that token.  ld_off = its byte offset inside the 32 rows.
+  // (physical ^ swz(token)) of that token.  ld_off = its byte offset inside the 32 rows;
+  // two offsets per register.  For a ragged stage (rows past tlast invalid) the rows past
+  // tlast re-read row tlast, so every LDS row holds finite cache data.
   uint32_t ld_off2[(kLoadsPerWave + 1) / 2];
+  auto set_ld_off = [&](int tlast) {
 #pragma unroll
-  for (int k = 0; k < 2 * ((kLoadsPerWave + 1) / 2); ++k) {
-    uint32_t o = 0;
-    if (k < kLoadsPerWave) {
-      const int Pc = 64 * (wave + kWaves * k) + lane;
-      const int t = Pc / kChunksPerRow;
-      const int pc = Pc % kChunksPerRow;
-      o = (uint32_t)(t * (kRow * 2) + (pc ^ swz(t)) * 16);
+    for (int k = 0; k < 2 * ((kLoadsPerWave + 1) / 2); ++k) {
+      uint32_t o = 0;
+      if (k < kLoadsPerWave) {
+        const int Pc = 64 * (wave + kWaves * k) + lane;
+        const int t = Pc / kChunksPerRow;
+        const int pc = Pc % kChunksPerRow;
+        o = (uint32_t)((t < tlast ? t : tlast) * (kRow * 2) + (pc ^ swz(t)) * 16);
+      }
+      if (k & 1) ld_off2[k >> 1] |= o << 16;
+      else ld_off2[k >> 1] = o;
     }
-    if (k & 1) ld_off2[k >> 1] |= o << 16;
-    else ld_off2[k >> 1] = o;
-  }
+  };
   auto ld_off = [&](int k) { return (k & 1) ? (ld_off2[k >> 1] >> 16) : (ld_off2[k >> 1] & 0xffffu); };
 
   // The block-table entry for token tok0 of sequence b: a scalar load whose
@@ -175,17 +179,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   // Issue all of this wave's copies of a stage into ring slot `slot` at once;
   // rows past tlast re-read row tlast (the last valid token), so every LDS row
   // holds finite cache data.
-  auto issue_stage = [&](int slot, uint64_t base, int tlast) {
+  auto issue_stage = [&](int slot, uint64_t base) {
     const uint32_t dst0 = (uint32_t)(uintptr_t)(lds + slot * kStageBytes + wave * 1024);
 #pragma unroll
-    for (int k = 0; k < kLoadsPerWave; ++k) {
-      uint32_t o = ld_off(k);
-      if (tlast < kSubTok - 1) {
-        const int r = (int)(o / (kRow * 2));
-        if (r > tlast) o -= (uint32_t)((r - tlast) * (kRow * 2));
-      }
-      copy16_to_lds(base, o, __builtin_amdgcn_readfirstlane(dst0 + kWaves * 1024 * k));
-    }
+    for (int k = 0; k < kLoadsPerWave; ++k)
+      copy16_to_lds(base, ld_off(k), __builtin_amdgcn_readfirstlane(dst0 + kWaves * 1024 * k));
   };
   // Copies that fetch nothing needed: an in-bounds read of the pool's first rows
   // into the spare kilobyte.  Every iteration issues the same number of copies,
@@ -242,8 +240,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     };
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
+      set_ld_off(k < nsub ? tlast_of(k) : kSubTok - 1);
       if (k < nsub) {
-        issue_stage(k, stage_base(lookup_block(b, a + k * kSubTok), a + k * kSubTok), tlast_of(k));
+        issue_stage(k, stage_base(lookup_block(b, a + k * kSubTok), a + k * kSubTok));
       } else {
         const uint32_t idle_dst = (uint32_t)(uintptr_t)(lds + k * kStageBytes + wave * 1024);
 #pragma unroll
@@ -271,11 +270,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       // iteration of this range reads it.
       uint64_t nbase = idle_base;
       uint32_t ndst = (uint32_t)(uintptr_t)(lds + ((it + 2) & 3) * kStageBytes + wave * 1024), nstride = 0;
-      int ntl = kSubTok - 1;   // last valid row of the stage fetched
       if (it + 2 < nsub) {
         nbase = stage_base(blk_next, a + (it + 2) * kSubTok);
         nstride = kWaves * 1024;
-        ntl = tlast_of(it + 2);
+        const int ntl = tlast_of(it + 2);
+        if (ntl < kSubTok - 1) set_ld_off(ntl);   // the range's last stage: later copies are idle
       }
       if (it + 3 < nsub) blk_next = lookup_block(b, a + (it + 3) * kSubTok);
       const bool valid = it < nsub;
@@ -312,14 +311,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
           if (ks + kPfS < 36) tv[ks % kPfS] = lds_read16(st + s_off[(ks + kPfS) & 3] + ((ks + kPfS) >> 2) * 128);
           if (ks == 0) mfma_s_first(acc_s, t, qreg[ks]);
           else mfma_s(acc_s, t, qreg[ks]);
-          if ((ks & 3) == 2) {
-            uint32_t o = ld_off(ks >> 2);
-            if (ntl < kSubTok - 1) {   // wave-uniform: only a sequence's last, ragged stage
-              const int r = (int)(o / (kRow * 2));
-              if (r > ntl) o -= (uint32_t)((r - ntl) * (kRow * 2));
-            }
-            copy16_to_lds(nbase, o, __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
-          }
+          if ((ks & 3) == 2)
+            copy16_to_lds(nbase, ld_off(ks >> 2), __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
           if (ks == 32) {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) pb[0][rb] = lds_read16(pp + rb * 2048);
