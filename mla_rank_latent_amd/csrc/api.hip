@@ -108,7 +108,8 @@ bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L
   L->off_wgseg = off; off += up((size_t)W * 4);
   L->off_qlat = off;  off += up((size_t)batch * sq * d->n_heads * R * elem_size(d->dtype));
   L->off_lse = off;   off += up((size_t)L->G * L->P * L->rows * 8);
-  L->off_o = off;     off += up((size_t)L->G * L->P * L->rows * d->d_latent * 4);
+  // partial latent sums: bf16 for the bf16 kernels, fp32 for the fp32 ones
+  L->off_o = off;     off += up((size_t)L->G * L->P * L->rows * d->d_latent * (bf ? 2 : 4));
   L->total = off;
   return true;
 }

@@ -68,5 +68,34 @@ __device__ __forceinline__ uint64_t uniform_addr(const void* p) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+
+// ---- Partial latent sums out of the accumulators: rounded to bf16, row-major [row][512].
+// The 128 rows go through LDS in passes of 32: the kernel writes a pass's fp32
+// accumulators to LDS straight from the AGPRs (stage_row_f4), then every thread
+// converts a few values at a time and stores whole 128-byte runs (store_pass_bf16).
+// Converting in registers instead would move all 256 accumulators into VGPRs at
+// once, which costs the main loop its registers.
+constexpr int kEpiRows = 32;
+constexpr int kEpiStride = kLat * 4 + 16;   // padded fp32 row in LDS
+static_assert(kEpiRows * kEpiStride <= 120 * 1024, "an epilogue pass fits the ring");
+
+// fp32 x4 of row r (0..31 within the pass), features f .. f + 3
+__device__ __forceinline__ void stage_row_f4(MLA_LDS uint8_t* lds, int r, int f, f32x4 v) {
+  *(MLA_LDS f32x4*)(lds + r * kEpiStride + f * 4) = v;
+}
+// 256 threads: the pass's 32 rows to out_rows[r * kLat ..] (bf16); row r is written only if
+// r < nrows
+__device__ __forceinline__ void store_pass_bf16(const MLA_LDS uint8_t* lds, uint16_t* out_rows, int tid) {
+  const int r = tid >> 3, part = tid & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int f = 8 * (8 * j + part);
+    const f32x4 a = *(const MLA_LDS f32x4*)(lds + r * kEpiStride + f * 4);
+    const f32x4 b = *(const MLA_LDS f32x4*)(lds + r * kEpiStride + f * 4 + 16);
+    *(u32x4*)(out_rows + (size_t)r * kLat + f) =
+        u32x4{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3])};
+  }
+}
+
 }  // namespace attn
 }  // namespace mla

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
   const MLA_CONST int32_t* btab = as_const(block_table);
   const uint16_t* q_lat = (const uint16_t*)(ws + Lw.off_qlat);
   float2* part_ml = (float2*)(ws + Lw.off_lse);
-  float* part_o = (float*)(ws + Lw.off_o);
+  uint16_t* part_o = (uint16_t*)(ws + Lw.off_o);   // bf16
 
   const int total = hdr->total;
   const int quota = hdr->quota;
@@ -448,14 +448,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
 
     // ---- partial state: un-normalised latent sum, reference max and weight sum
     const float l_tot = l_sum + __shfl_xor(l_sum, 32);
-    float* op = part_o + ((size_t)piece * kRowsWG + row) * kLat + 4 * hh;
+    // (rounded to bf16 on the way out, through LDS in passes of 32 rows: pass p holds wave
+    // p's rows; the ring is free once every wave has left the loop)
+    uint16_t* prow = part_o + (size_t)piece * kRowsWG * kLat;
 #pragma unroll
-    for (int fb = 0; fb < 16; ++fb) {
+    for (int pass = 0; pass < kRowsWG / kEpiRows; ++pass) {
+      if (wave == pass) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 v = {acc_o[fb][4 * rr], acc_o[fb][4 * rr + 1], acc_o[fb][4 * rr + 2], acc_o[fb][4 * rr + 3]};
-        *(f32x4*)(op + fb * 32 + 8 * rr) = v;
+        for (int fb = 0; fb < 16; ++fb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            stage_row_f4(lds, n, 32 * fb + 8 * rr + 4 * hh,
+                         f32x4{acc_o[fb][4 * rr], acc_o[fb][4 * rr + 1], acc_o[fb][4 * rr + 2], acc_o[fb][4 * rr + 3]});
       }
+      __syncthreads();
+      store_pass_bf16(lds, prow + (size_t)kEpiRows * pass * kLat, tid);
+      __syncthreads();   // LDS free for the next pass (or the next range)
     }
     if (hh == 0) part_ml[(size_t)piece * kRowsWG + row] = make_float2(m_ref, l_tot);
   }

@@ -2,8 +2,8 @@
 // gfx950 bf16 MFMA with fp32 accumulate.
 //
 // Each range of cached tokens left, per query row, an un-normalised latent
-// sum O_k = sum_j 2^(z_j - m_k) c_j with its reference m_k and weight sum
-// l_k (log2 units).  The exact merge is
+// sum O_k = sum_j 2^(z_j - m_k) c_j (bf16) with its reference m_k and weight
+// sum l_k (log2 units).  The exact merge is
 //   M = max_k m_k,  w_k = 2^(m_k - M),
 //   o_lat = sum_k w_k O_k / sum_k w_k l_k,   lse = ln 2 * (M + log2 sum_k w_k l_k).
 // Then the value side of matrix absorption ("DeepSeek-V2: Multi-Head Latent
@@ -13,8 +13,8 @@
 //
 // One workgroup of eight waves per (head, 32 query rows).
 //  - Merge: sixteen threads per row, each owning 32 of its 512 columns
-//    (16 bytes at 256-byte strides, so the sixteen lanes of a row read whole
-//    256-byte blocks).  Two pieces' loads are in flight per thread and the
+//    (8 bytes at 128-byte strides, so the sixteen lanes of a row read whole
+//    128-byte blocks).  Two pieces' loads are in flight per thread and the
 //    piece weights are applied branch-free, so the partial states stream at
 //    memory rate instead of one round trip per piece.
 //  - The merged latent goes to LDS as a bf16 high part and a bf16 remainder
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     float den = 0.0f, Mx = -__builtin_inff();
     int p0 = 0, p1 = 0, r = 0;
     const float2* part_ml = (const float2*)(ws + Lw.off_lse);
-    const float* part_o = (const float*)(ws + Lw.off_o);
+    const uint16_t* part_o = (const uint16_t*)(ws + Lw.off_o);   // bf16
     if (row_ok) {
       const int b = m / sq;
       const int s = m - b * sq;
@@ -122,13 +122,23 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
         const int q = p + pl_n < p1 ? p + pl_n : p;
         const float2 ml0 = part_ml[(size_t)p * Lw.rows + r];
         const float2 ml1 = part_ml[(size_t)q * Lw.rows + r];
-        const f32x4* o0 = (const f32x4*)(part_o + ((size_t)p * Lw.rows + r) * kLat) + c16;
-        const f32x4* o1 = (const f32x4*)(part_o + ((size_t)q * Lw.rows + r) * kLat) + c16;
+        const u32x2* o0 = (const u32x2*)(part_o + ((size_t)p * Lw.rows + r) * kLat) + c16;
+        const u32x2* o1 = (const u32x2*)(part_o + ((size_t)q * Lw.rows + r) * kLat) + c16;
+        u32x2 b0[8], b1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b0[j] = o0[16 * j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b1[j] = o1[16 * j];
+        auto widen = [](u32x2 b) {
+          return f32x4{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xffff0000u), __uint_as_float(b[1] << 16),
+                       __uint_as_float(b[1] & 0xffff0000u)};
+        };
         f32x4 v0[8], v1[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v0[j] = o0[16 * j];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v1[j] = o1[16 * j];
+        for (int j = 0; j < 8; ++j) {
+          v0[j] = widen(b0[j]);
+          v1[j] = widen(b1[j]);
+        }
         // an empty piece has l = 0, m = -inf and O = 0: weight 0
         const float w0 = ml0.y > 0.0f ? __builtin_amdgcn_exp2f(ml0.x - Mx) : 0.0f;
         const float w1 = (q != p && ml1.y > 0.0f) ? __builtin_amdgcn_exp2f(ml1.x - Mx) : 0.0f;

@@ -57,8 +57,8 @@ def test_cache_bytes_accounting():
 def test_workspace_query():
     v2 = mla.dims(128, 128, 64, 512, 5120)
     w64 = mla.mla_decode_workspace_bytes(v2, 64, 1, 256)
-    # q_lat + (256 + 64) pieces x 128 rows x (512 floats + 2 floats) + plan
-    assert w64 >= 64 * 128 * 576 * 2 + 320 * 128 * 514 * 4
+    # q_lat + (256 + 64) pieces x 128 rows x (512 bf16 latent sums + 2 floats) + plan
+    assert w64 >= 64 * 128 * 576 * 2 + 320 * 128 * (512 * 2 + 8)
     assert mla.mla_decode_workspace_bytes(v2, 64, 2, 128) > 0
     assert mla.mla_decode_workspace_bytes(v2, 64, 9, 128) == 0     # sq beyond the bf16 kernels
     assert mla.mla_decode_workspace_bytes(v2, 0, 1, 128) == 0
