@@ -106,17 +106,8 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
       const int32_t* piece_base = (const int32_t*)(ws + Lw.off_piece);
       p0 = g * P + piece_base[b];
       p1 = g * P + piece_base[b + 1];
-      for (int p = p0 + pl; p < p1; p += pl_n) {
-        const float2 ml = part_ml[(size_t)p * Lw.rows + r];
-        if (ml.y > 0.0f) Mx = fmaxf(Mx, ml.x);
-      }
-    }
-    if (pl_n > 1) {   // the row's maximum over all of its slots
-      if (c16 == 0) s_mx[slot] = Mx;
-      __syncthreads();
-      for (int q = 0; q < pl_n; ++q) Mx = fmaxf(Mx, s_mx[q * rp + i]);
-    }
-    if (row_ok && Mx != -__builtin_inff()) {
+      // online merge: the running maximum rises as pieces arrive and the sums so far are
+      // rescaled, so each pair's loads (states and weights together) need one round trip
       for (int p = p0 + pl; p < p1; p += 2 * pl_n) {
         // the second piece of the pair; past the end it re-reads piece p with weight 0
         const int q = p + pl_n < p1 ? p + pl_n : p;
@@ -129,23 +120,34 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
         for (int j = 0; j < 8; ++j) b0[j] = o0[16 * j];
 #pragma unroll
         for (int j = 0; j < 8; ++j) b1[j] = o1[16 * j];
-        auto widen = [](u32x2 b) {
-          return f32x4{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xffff0000u), __uint_as_float(b[1] << 16),
-                       __uint_as_float(b[1] & 0xffff0000u)};
+        // an empty piece has l = 0 (m = -inf, O = 0): weight 0
+        const float m0 = ml0.y > 0.0f ? ml0.x : -__builtin_inff();
+        const float m1 = (q != p && ml1.y > 0.0f) ? ml1.x : -__builtin_inff();
+        const float mn = fmaxf(Mx, fmaxf(m0, m1));
+        if (mn == -__builtin_inff()) continue;   // nothing seen yet
+        const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - mn);
+        const float w0 = m0 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m0 - mn);
+        const float w1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mn);
+        auto widen = [](u32x2 v) {
+          return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+                       __uint_as_float(v[1] & 0xffff0000u)};
         };
-        f32x4 v0[8], v1[8];
+        den = den * sc + w0 * ml0.y + w1 * ml1.y;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          v0[j] = widen(b0[j]);
-          v1[j] = widen(b1[j]);
-        }
-        // an empty piece has l = 0, m = -inf and O = 0: weight 0
-        const float w0 = ml0.y > 0.0f ? __builtin_amdgcn_exp2f(ml0.x - Mx) : 0.0f;
-        const float w1 = (q != p && ml1.y > 0.0f) ? __builtin_amdgcn_exp2f(ml1.x - Mx) : 0.0f;
-        den += w0 * ml0.y + w1 * ml1.y;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += w0 * v0[j] + w1 * v1[j];
+        for (int j = 0; j < 8; ++j) acc[j] = acc[j] * sc + w0 * widen(b0[j]) + w1 * widen(b1[j]);
+        Mx = mn;
       }
+    }
+    if (pl_n > 1) {   // bring the row's slots to the row's maximum
+      if (c16 == 0) s_mx[slot] = Mx;
+      __syncthreads();
+      float Mg = Mx;
+      for (int q = 0; q < pl_n; ++q) Mg = fmaxf(Mg, s_mx[q * rp + i]);
+      const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - Mg);
+      den *= sc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= sc;
+      Mx = Mg;
     }
     if (pl_n > 1) {   // sum the row's slots in slot order
       MLA_LDS f32x4* comb = (MLA_LDS f32x4*)s_comb;
