@@ -214,18 +214,18 @@ __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __
   const int col = 2 * (int)(idx % (kRow / 2));
   const float* pp = part + (size_t)tok * nslice * kRow + col;
   float v0 = 0.0f, v1 = 0.0f;
-  for (int s0 = 0; s0 < nslice; s0 += 8) {
-    float2 p[8];
+  const int pos = positions[tok];   // issued with the partial sums: one memory round trip
+  for (int s0 = 0; s0 < nslice; s0 += 16) {
+    float2 p[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = *(const float2*)(pp + (size_t)(s0 + u < nslice ? s0 + u : s0) * kRow);
+    for (int u = 0; u < 16; ++u) p[u] = *(const float2*)(pp + (size_t)(s0 + u < nslice ? s0 + u : s0) * kRow);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
       if (s0 + u < nslice) {
         v0 += p[u].x;
         v1 += p[u].y;
       }
   }
-  const int pos = positions[tok];
   uint16_t* dst = append_dst(cache, block_table, max_blocks, num_blocks, tok, t_per_seq, pos, status);
   if (dst == nullptr) return;
   uint32_t outv;
