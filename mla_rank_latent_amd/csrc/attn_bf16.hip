@@ -169,12 +169,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   };
   // Global address of the 32-token stage starting at token tok0, inside cache
   // block blk.  A block id outside the pool is reported and replaced by block 0.
+  const uint64_t cache_u = uniform_addr(cache);
   auto stage_base = [&](int blk, int tok0) {
-    if (blk < 0 || blk >= num_blocks) {
-      if (lane == 0 && status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
-      blk = 0;
-    }
-    return uniform_addr((const uint8_t*)cache + ((size_t)blk * kBlk + (tok0 % kBlk)) * (size_t)(kRow * 2));
+    const bool bad = blk < 0 || blk >= num_blocks;   // wave-uniform; the address math stays scalar
+    if (bad && lane == 0 && status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
+    const uint32_t row = (uint32_t)(bad ? 0 : blk) * kBlk + (uint32_t)(tok0 % kBlk);
+    return cache_u + (uint64_t)__builtin_amdgcn_readfirstlane(row) * (uint64_t)(kRow * 2);
   };
   // Issue all of this wave's copies of a stage into ring slot `slot` at once;
   // rows past tlast re-read row tlast (the last valid token), so every LDS row
