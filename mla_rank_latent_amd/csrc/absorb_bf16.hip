@@ -136,7 +136,6 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
     bop[ks] = u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
   }
 
-  const int col = cb * 128 + 32 * wave + n;
   for (int mb = 0; mb < nmb; ++mb) {
     if (mb + 1 < nmb) stage_q(mb + 1);   // the next block lands while this one is multiplied
     const MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
@@ -150,13 +149,18 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __rest
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const u32x4 a = *(const MLA_LDS u32x4*)(qb + r * (kNope * 2) + (((2 * ks + hh) ^ (r & 15)) * 16));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(bop[ks]), acc, 0, 0, 0);
+        // operands in swapped roles: the product is D^T, [column x query row]
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(a), acc, 0, 0, 0);
       }
-      // D[m][col]: lane holds column 32 wave + n, rows 8 (i/4) + 4 hh + i % 4
+      // D^T: lane holds query row 32 half + n, columns 32 wave + 8 (i/4) + 4 hh + i % 4, so
+      // each group of four registers is four adjacent columns: one 8-byte store
+      const int mm = mb * 64 + 32 * half + n;
+      if (mm < M) {
+        uint16_t* dst = q_lat + ((size_t)mm * n_heads + h) * kRow + cb * 128 + 32 * wave + 4 * hh;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int mm = mb * 64 + 32 * half + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (mm < M) q_lat[((size_t)mm * n_heads + h) * kRow + col] = f2bf(acc[i] * qscale);
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale),
+                                          pack_bf2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale)};
       }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // next block landed (and this block's stores issued)

@@ -69,7 +69,9 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
   int32_t* piece = (int32_t*)(ws + Lw.off_piece);
   int32_t* wgseg = (int32_t*)(ws + Lw.off_wgseg);
   const int t = threadIdx.x;
-  // pass 1: prefix sums of rounded lengths -> seg_start, and the total
+  // pass 1: prefix sums of rounded lengths -> seg_start, and the total.  With at most 256
+  // sequences each thread keeps its segment for pass 2 instead of reading it back.
+  int my_s0 = 0, my_s1 = 0;
   if (t == 0) s_carry = 0;
   __syncthreads();
   for (int base = 0; base < batch; base += 256) {
@@ -87,7 +89,11 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
       s_scan[t] += add;
       __syncthreads();
     }
-    if (b < batch) seg[b] = s_carry + s_scan[t] - v;
+    if (b < batch) {
+      my_s0 = s_carry + s_scan[t] - v;
+      my_s1 = my_s0 + v;
+      seg[b] = my_s0;
+    }
     __syncthreads();
     if (t == 255) s_carry += s_scan[255];
     __syncthreads();
@@ -105,8 +111,8 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
     int b = base + t;
     int v = 0, s0 = 0, s1 = 0;
     if (b < batch) {
-      s0 = seg[b];
-      s1 = seg[b + 1];
+      s0 = batch <= 256 ? my_s0 : seg[b];
+      s1 = batch <= 256 ? my_s1 : seg[b + 1];
       v = s1 > s0 ? (s1 - 1) / quota - s0 / quota + 1 : 0;
     }
     s_scan[t] = v;
