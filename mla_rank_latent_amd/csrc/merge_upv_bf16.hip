@@ -19,10 +19,12 @@
 //    memory rate instead of one round trip per piece.
 //  - The merged latent goes to LDS as a bf16 high part and a bf16 remainder
 //    (two MFMAs per step keep the product close to fp32 accuracy).
-//  - Up-projection [32 x 512] . [512 x 128] on MFMA 32x32x16: wave (kh, wc)
-//    takes output columns 32 wc .. 32 wc + 31 over latent half kh, with its
-//    W^UV slice loaded into registers before the merge starts; the two
-//    latent halves are summed through LDS.
+//  - Up-projection [32 x 512] . [512 x 128] on MFMA 32x32x16, computed
+//    transposed so that each lane ends with four adjacent output columns per
+//    register group (8-byte stores): wave (kh, wc) takes output columns
+//    32 wc .. 32 wc + 31 over latent half kh, with its W^UV slice loaded into
+//    registers before the merge starts; the two latent halves are summed
+//    through LDS.
 #include "device_util.h"
 
 namespace mla {
@@ -198,22 +200,29 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     const int off = n * (kLat * 2) + ((chunk & ~7) | ((chunk & 7) ^ (n & 7))) * 16;
     const u32x4 ah = *(const MLA_LDS u32x4*)(s_hi + off);
     const u32x4 al = *(const MLA_LDS u32x4*)(s_lo + off);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ah), as_bf8(bop[ks]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(al), as_bf8(bop[ks]), acc, 0, 0, 0);
+    // operands in swapped roles: the product is out^T, [output column x row]
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(ah), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(al), acc, 0, 0, 0);
   }
-  // D layout: register r holds row 8 (r / 4) + 4 hh + r % 4, column n
+  // out^T layout: lane holds row n, register r column 32 wc + 8 (r / 4) + 4 hh + r % 4, so each
+  // group of four registers is four adjacent columns
   if (kh == 1) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_red[(8 * (r >> 2) + 4 * hh + (r & 3)) * kNope + 32 * wc + n] = acc[r];
+    for (int g = 0; g < 4; ++g)
+      *(MLA_LDS f32x4*)(s_red + n * kNope + 32 * wc + 8 * g + 4 * hh) =
+          f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
   }
   __syncthreads();
   if (kh == 0) {
-    const int d = 32 * wc + n;
+    const int m = mb * kMergeRows + n;
+    if (m < M) {
+      uint16_t* dst = out + ((size_t)m * n_heads + h) * kNope + 32 * wc + 4 * hh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-      const int m = mb * kMergeRows + row;
-      if (m < M) out[((size_t)m * n_heads + h) * kNope + d] = f2bf(acc[r] + s_red[row * kNope + d]);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o = *(const MLA_LDS f32x4*)(s_red + n * kNope + 32 * wc + 8 * g + 4 * hh);
+        *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] + o[0], acc[4 * g + 1] + o[1]),
+                                        pack_bf2(acc[4 * g + 2] + o[2], acc[4 * g + 3] + o[3])};
+      }
     }
   }
 }
