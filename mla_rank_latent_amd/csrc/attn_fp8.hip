@@ -319,9 +319,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
       const MLA_LDS uint8_t* sto = lds + ((it > 0 ? it - 1 : 0) % kQSlots) * kQStage;
       const int tok0 = a + it * kSubTok;
 
-      // ---- S^T = T . Q^T (32 tokens x 32 rows): 16 code pairs and 4 k^R k-steps, even and odd
-      // k-steps in two chains.  Lane n's operands are token n's, scaled by its s_n.
-      f32x16 acc_s, acc_s1;
+      // ---- S^T = T . Q^T (32 tokens x 32 rows): 16 code pairs and 4 k^R k-steps in one
+      // accumulation chain (dependent MFMAs of one opcode issue back to back).  Lane n's
+      // operands are token n's, scaled by its s_n.
+      f32x16 acc_s;
       {
         const float s_n = *(const MLA_LDS float*)(st + kQScale + 4 * n);
         u32x4 tv[kPfS];
@@ -339,23 +340,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
           const u32x2 c2 = cvt4(raw[2], s_n), c3 = cvt4(raw[3], s_n);
           const u32x4 opa = {c0[0], c0[1], c1[0], c1[1]};
           const u32x4 opb = {c2[0], c2[1], c3[0], c3[1]};
-          if (j == 0) {
-            mfma_sv_first(acc_s, opa, qreg[0]);
-            mfma_sv_first(acc_s1, opb, qreg[1]);
-          } else {
-            mfma_sv(acc_s, opa, qreg[2 * j]);
-            mfma_sv(acc_s1, opb, qreg[2 * j + 1]);
-          }
+          if (j == 0) mfma_sv_first(acc_s, opa, qreg[0]);
+          else mfma_sv(acc_s, opa, qreg[0 + 2 * j]);
+          mfma_sv(acc_s, opb, qreg[2 * j + 1]);
           if ((j & 3) == 1) {
             // a k^R k-step every fourth pair, alternating chains
             const int k = j >> 2;
             const u32x4 r = rv;
             if (k < 3) rv = lds_read16(st + (sr_off ^ (32 * (k + 1))));
-            mfma_s(k & 1 ? acc_s1 : acc_s, r, lds_read16(lds + (qr_off ^ (32 * k))));
+            mfma_s(acc_s, r, lds_read16(lds + (qr_off ^ (32 * k))));
           }
           if (j >= 2 && j < 2 + 2 * kQCopies && (j & 1) == 0) copy_i(nt, (j - 2) >> 1, kSubTok - 1);
         }
-        settle_s(acc_s, acc_s1);
+        settle_s(acc_s);
       }
 
       // ---- softmax weights of stage it against the row reference (log2 units), interleaved
@@ -365,7 +362,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
       {
         float z[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = (acc_s[r] + acc_s1[r]) * zscale;
+        for (int r = 0; r < 16; ++r) z[r] = acc_s[r] * zscale;
         float sc[16];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
