@@ -18,9 +18,12 @@
 // bf16 as the bf16 kernel's p_j do).
 //
 // Mapping onto the chip: as the bf16 kernel (128 query rows per workgroup, four
-// waves of 32 rows, MFMA 32x32x16 bf16 for both products, the score MFMAs in
-// their VGPR form, the latent product of stage it - 1 interleaved with stage
-// it's softmax, restart-on-overflow reference).  What the format changes:
+// waves, one per SIMD: a wave scores its own 32 rows and accumulates its quarter
+// of the 512 latent features for all 128 rows, with the bf16 weights shared
+// through LDS; MFMA 32x32x16 bf16 for both products, the score MFMAs in their
+// VGPR form in one chain, the latent product of stage it - 1 interleaved step by
+// step with stage it's softmax, restart-on-overflow reference).  What the
+// format changes:
 //  - A 32-token stage is 21 KB instead of 36 KB (16 KB of codes, 4 KB of k^R,
 //    the 128 B of scales in a 1 KB slot), so the ring holds six stages and
 //    four are in flight while one is scored and one multiplied.
@@ -31,6 +34,8 @@
 //  - Latent-product operands come from ds_read_b64_tr_b8, which hands each
 //    lane one feature of eight tokens (the order in which the score result
 //    holds its tokens), converted with scale 1; the scale rides on the weight.
+//    A wave converts only its feature quarter, and each converted operand
+//    feeds the four row blocks' MFMAs.
 //  - LDS rows: 16-byte chunk c of a token's 512-byte code row sits at
 //    c ^ swf(t), swf a permutation of t's low four bits chosen so that the
 //    16 tokens of a score read and the 8 tokens x 2 chunks of a transposing
@@ -55,10 +60,11 @@ constexpr int kQSlots = 6;                       // ring slots
 constexpr int kQAhead = kQSlots - 2;             // stages in flight
 constexpr int kQCopies = 6;                      // 1 KB copies per wave and stage (21 used of 24)
 constexpr int kPfS = 3;                          // score reads ahead (each feeds two k-steps)
-constexpr int kPfO = 5;                          // latent-product reads ahead
 constexpr int kQIdle = kQSlots * kQStage;       // the spare kilobyte
 constexpr int kQRq = kQIdle + 1024;              // q^R of the 128 rows (128 B each)
-constexpr int kQLds = kQRq + kRowsWG * kRope * 2;
+constexpr int kPBytes = kRowsWG * kSubTok * 2;   // one stage's weights for all rows: 8 KB
+constexpr int kQP = kQRq + kRowsWG * kRope * 2;   // two slots of softmax weights (bf16)
+constexpr int kQLds = kQP + 2 * kPBytes;
 static_assert(kQStage % 1024 == 0 && kQLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int swf(int t) { return ((t & 3) << 1) | ((t >> 2) & 1) | (t & 8); }
@@ -292,7 +298,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
     // block ids are looked up one stage ahead of their copies
     int blk_next = kQAhead < nsub ? lookup_block(b, a + kQAhead * kSubTok) : 0;
     // softmax weights (times scales) of the previous stage, bf16 pairs, consumed one iteration later
-    uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    // the weights of the (empty) stage before the first: zero
+    *(MLA_LDS u32x4*)(lds + kQP + kPBytes + wave * 2048 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    *(MLA_LDS u32x4*)(lds + kQP + kPBytes + wave * 2048 + 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
 
     for (int it = 0; it <= nsub; ++it) {
       // This wave's copies of stage it have landed once at most kQAhead - 1 stages' worth
@@ -355,21 +363,24 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
         settle_s(acc_s);
       }
 
-      // ---- softmax weights of stage it against the row reference (log2 units), interleaved
-      // below with the latent product of stage it - 1.  Lane holds row n and tokens
-      // 8 (r / 4) + 4 hh + r % 4, r = 0..15, whose scales it reads here.
+      // ---- softmax weights of stage it against the row reference (log2 units; lane holds row
+      // n and tokens 8 (r / 4) + 4 hh + r % 4, r = 0..15, whose scales it reads here),
+      // interleaved step by step with the latent product of stage it - 1:
+      //   O^T += C^T . (P S)^T over this wave's 128 features (4 blocks of 32) x all 128 rows
+      //   (4 row blocks) x 2 token halves, 32 MFMAs.  The weights come from LDS, written
+      //   there by the wave that owns each row block; each converted tile operand feeds
+      //   four MFMAs.
       uint32_t pk[8];
       {
-        float z[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = acc_s[r] * zscale;
-        float sc[16];
+        float z[16], sc[16];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const f32x4 v = *(const MLA_LDS f32x4*)(st + kQScale + 4 * (8 * qd + 4 * hh));
 #pragma unroll
           for (int c = 0; c < 4; ++c) sc[4 * qd + c] = v[c];
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = acc_s[r];
         if (!valid || tok0 + kSubTok - 1 > L - sq) {   // past some row's last visible token, or no stage
           asm volatile("");   // a branch taken on a sequence's last stage only: keep it one
 #pragma unroll
@@ -380,54 +391,61 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
             sc[r] = off ? 0.0f : sc[r];   // a slot past the sequence may hold any bits
           }
         }
-        float mx = z[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, z[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        m_run = fmaxf(m_run, mx);
-        m_ref = m_ref == kNegInf ? mx : m_ref;   // a row's reference: its first finite stage maximum
-        bad = bad || (mx > m_ref + kLazyTau);
-        const float msafe = m_ref == kNegInf ? 0.0f : m_ref;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(z[r] - msafe);
-          const float p1 = __builtin_amdgcn_exp2f(z[r + 1] - msafe);
-          l_sum += p0 + p1;
-          pk[r >> 1] = pack_bf2(p0 * sc[r], p1 * sc[r + 1]);
-        }
-      }
-
-      // ---- O^T += C^T . (P S)^T for stage it - 1 (512 features x 32 rows): 16 feature blocks
-      // x 2 token halves
-      {
-        const u32x4 pb0 = {pk_prev[0], pk_prev[1], pk_prev[2], pk_prev[3]};
-        const u32x4 pb1 = {pk_prev[4], pk_prev[5], pk_prev[6], pk_prev[7]};
-        auto rd = [&](int j) {
-          const int fb = j & 15, hs = j >> 4;
-          return lds_read_tr8(sto + ((o8_off ^ (32 * (fb & 7))) + 256 * (fb >> 3) + hs * (16 * kLat)));
-        };
-        u32x2 av[kPfO];
-#pragma unroll
-        for (int k = 0; k < kPfO; ++k) av[k] = rd(k);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const u32x2 raw = av[j % kPfO];
-          if (j + kPfO < 32) av[j % kPfO] = rd(j + kPfO);
+        const MLA_LDS uint8_t* pp = lds + kQP + ((it + 1) & 1) * kPBytes + lane * 16;
+        // A operand a = 4 hs + fb: feature block 4 wave + fb, token half hs
+        auto rd = [&](int a) {
+          const int hs = a >> 2, FB = 4 * wave + (a & 3);
+          const u32x2 raw = lds_read_tr8(sto + ((o8_off ^ (32 * (FB & 7))) + 256 * (FB >> 3) + hs * (16 * kLat)));
           const u32x2 c0 = cvt4(raw[0], 1.0f), c1 = cvt4(raw[1], 1.0f);
-          const u32x4 op = {c0[0], c0[1], c1[0], c1[1]};
-          acc_o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(op), as_bf8(j < 16 ? pb0 : pb1),
-                                                                  acc_o[j & 15], 0, 0, 0);
-        }
+          return u32x4{c0[0], c0[1], c1[0], c1[1]};
+        };
+        u32x4 pb[2][4], av[8];
 #pragma unroll
-        for (int k = 0; k < kPfO; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int rb = 0; rb < 4; ++rb) pb[0][rb] = lds_read16(pp + rb * 2048);
+        av[0] = rd(0);
+        av[1] = rd(1);
+        float mx = 0.0f, msafe = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (j + kPfO < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int jj = 0; jj < 32; ++jj) {
+          const int hs = jj >> 4, fb = (jj >> 2) & 3, rb = jj & 3, ai = 4 * hs + fb;
+          acc_o[4 * fb + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(av[ai]), as_bf8(pb[hs][rb]),
+                                                                       acc_o[4 * fb + rb], 0, 0, 0);
+          if (rb == 0 && ai + 2 < 8) av[ai + 2] = rd(ai + 2);
+          if (jj == 8) {
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) pb[1][r2] = lds_read16(pp + r2 * 2048 + 1024);
+          }
+          if (jj == 0) {
+            mx = __builtin_fmaxf(__builtin_fmaxf(z[0], __builtin_fmaxf(z[1], z[2])),
+                                 __builtin_fmaxf(__builtin_fmaxf(z[3], __builtin_fmaxf(z[4], z[5])), __builtin_fmaxf(z[6], z[7])));
+          } else if (jj == 1) {
+            mx = fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(z[8], __builtin_fmaxf(z[9], z[10])),
+                                           __builtin_fmaxf(__builtin_fmaxf(z[11], __builtin_fmaxf(z[12], z[13])),
+                                                           __builtin_fmaxf(z[14], z[15]))));
+          } else if (jj == 2) {
+            // the other lane half holds the same row's other 16 tokens
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * zscale;   // zscale > 0
+            m_run = fmaxf(m_run, mx);
+            m_ref = m_ref == kNegInf ? mx : m_ref;   // a row's reference: its first finite stage maximum
+            bad = bad || (mx > m_ref + kLazyTau);
+            msafe = m_ref == kNegInf ? 0.0f : m_ref;
+          } else if (jj >= 3 && jj < 27 && (jj - 3) % 3 == 0) {
+            const int r = 2 * ((jj - 3) / 3);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[r], zscale, -msafe));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[r + 1], zscale, -msafe));
+            l_sum += p0 + p1;
+            pk[r >> 1] = pack_bf2(p0 * sc[r], p1 * sc[r + 1]);
+          } else if (jj == 27) {
+            // this stage's weights, for every wave's latent product in the next iteration
+            MLA_LDS uint8_t* pw = lds + kQP + (it & 1) * kPBytes + wave * 2048 + lane * 16;
+            *(MLA_LDS u32x4*)pw = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            *(MLA_LDS u32x4*)(pw + 1024) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) pk_prev[k] = pk[k];
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0ull && lane == 0) s_retry = 1;
     __syncthreads();   // ring free for the next range; every wave's flag visible
@@ -445,18 +463,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
 
     // ---- partial state: un-normalised latent sum, reference max and weight sum
     const float l_tot = l_sum + __shfl_xor(l_sum, 32);
-    // (rounded to bf16 on the way out, through LDS in passes of 32 rows: pass p holds wave
-    // p's rows; the ring is free once every wave has left the loop)
+    // (rounded to bf16 on the way out, through LDS in passes of 32 rows, one row block each;
+    // the ring is free once every wave has left the loop)
     uint16_t* prow = part_o + (size_t)piece * kRowsWG * kLat;
 #pragma unroll
     for (int pass = 0; pass < kRowsWG / kEpiRows; ++pass) {
-      if (wave == pass) {
 #pragma unroll
-        for (int fb = 0; fb < 16; ++fb)
+      for (int fb = 0; fb < 4; ++fb) {
+        const f32x16& A = acc_o[4 * fb + pass];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            stage_row_f4(lds, n, 32 * fb + 8 * rr + 4 * hh,
-                         f32x4{acc_o[fb][4 * rr], acc_o[fb][4 * rr + 1], acc_o[fb][4 * rr + 2], acc_o[fb][4 * rr + 3]});
+        for (int rr = 0; rr < 4; ++rr)
+          stage_row_f4(lds, n, 128 * wave + 32 * fb + 8 * rr + 4 * hh,
+                       f32x4{A[4 * rr], A[4 * rr + 1], A[4 * rr + 2], A[4 * rr + 3]});
       }
       __syncthreads();
       store_pass_bf16(lds, prow + (size_t)kEpiRows * pass * kLat, tid);
