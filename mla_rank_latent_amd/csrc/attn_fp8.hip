@@ -210,15 +210,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
   const uint32_t idle_dst = (uint32_t)(uintptr_t)(lds + kQIdle);
   const Target idle_target{idle_base, idle_base, idle_base, idle_dst, 0u, idle_dst};
   auto target_of = [&](int blk, int tok0, int slot) {
-    if (blk < 0 || blk >= num_blocks) {
-      if (lane == 0 && status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
-      blk = 0;
-    }
-    const int half = (tok0 % kBlk) / kSubTok;
-    const uint8_t* pg = pages + (size_t)blk * kFp8PageBytes;
+    const bool bad = blk < 0 || blk >= num_blocks;   // wave-uniform; the address math stays scalar
+    if (bad && lane == 0 && status) atomicOr(status, MLA_STATUS_BAD_BLOCK);
+    const uint32_t ub = __builtin_amdgcn_readfirstlane((uint32_t)(bad ? 0 : blk));
+    const uint32_t half = (uint32_t)((tok0 % kBlk) / kSubTok);
+    const uint64_t pg = idle_base + (uint64_t)ub * (uint64_t)kFp8PageBytes;
     const uint32_t d0 = (uint32_t)(uintptr_t)(lds + slot * kQStage + 1024 * wave);
-    return Target{uniform_addr(pg + half * kQLat), uniform_addr(pg + kFp8RopeOff + half * kQRope),
-                  wave == 0 ? uniform_addr(pg + kFp8ScaleOff + half * (kSubTok * 4)) : idle_base, d0,
+    return Target{pg + half * kQLat, pg + kFp8RopeOff + half * kQRope,
+                  wave == 0 ? pg + kFp8ScaleOff + half * (kSubTok * 4) : idle_base, d0,
                   (uint32_t)(kWaves * 1024), wave == 0 ? d0 + kWaves * 1024 * 5 : idle_dst};
   };
   // Copy i of this wave; with tlast < 31 (a sequence's last stage) rows past tlast re-read row
