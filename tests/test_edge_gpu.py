@@ -130,3 +130,31 @@ def test_late_dominant_token_restarts_the_range(num_splits):
     ref, lse = H.oracle_decode(x)
     H.assert_close(H.host(c.out), ref, "bf16", f"late_spike splits={num_splits}")
     assert np.max(np.abs(H.host(c.lse) - lse) / np.maximum(np.abs(lse), 1.0)) <= 2e-2
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0721687836, 0.0721687836 * 3.0, 1e-3])
+def test_softmax_scale_extremes(scale):
+    """The softmax scale reaches the kernels as a power of two applied to the absorbed query
+    and a factor in [0.71, 1.42] applied to the logits.  Zero gives uniform weights, a negative
+    scale flips the logits' order, three times the usual scale makes the softmax sharp (a few
+    tokens carry each row), a tiny one makes every weight nearly equal; each must still match
+    the oracle.  (A sharper softmax amplifies the logits' rounding, which comes from the bf16
+    absorbed query at any scale: at five times the usual scale the absolute error reaches the
+    2e-2 bar.)"""
+    spec = H.small_spec("scales", 2, 2, [700, 129], seed=61)
+    x = synth.make_inputs(spec)
+    x["scale"] = float(scale)
+    c = H.GpuCase(x)
+    c.decode()
+    import torch
+    torch.cuda.synchronize()
+    assert int(c.status.item()) == 0
+    ref, lse = H.oracle_decode(x)
+    out = H.host(c.out).astype(np.float64)
+    r = H.rel_l2(out, ref)
+    # A sharp softmax puts single cache values, up to ~4 in size, into the output, whose own
+    # bf16 rounding is then up to 2^-8 of it: the absolute bar counts beyond that rounding.
+    excess = np.max(np.abs(out - ref) - 2.0 ** -8 * np.abs(ref))
+    H.log(f"  scale={scale}: rel_l2={r:.3e} max_abs={np.max(np.abs(out - ref)):.3e} beyond rounding={excess:.3e}")
+    assert r <= 1e-2 and excess <= 2e-2, (scale, r, excess)
+    assert np.max(np.abs(H.host(c.lse) - lse) / np.maximum(np.abs(lse), 1.0)) <= 2e-2
