@@ -176,9 +176,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     const uint32_t row = (uint32_t)(bad ? 0 : blk) * kBlk + (uint32_t)(tok0 % kBlk);
     return cache_u + (uint64_t)__builtin_amdgcn_readfirstlane(row) * (uint64_t)(kRow * 2);
   };
-  // Issue all of this wave's copies of a stage into ring slot `slot` at once;
-  // rows past tlast re-read row tlast (the last valid token), so every LDS row
-  // holds finite cache data.
+  // Issue all of this wave's copies of a stage into ring slot `slot` at once, with the
+  // offsets set_ld_off last produced (clamped for a ragged stage).
   auto issue_stage = [&](int slot, uint64_t base) {
     const uint32_t dst0 = (uint32_t)(uintptr_t)(lds + slot * kStageBytes + wave * 1024);
 #pragma unroll
@@ -186,8 +185,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       copy16_to_lds(base, ld_off(k), __builtin_amdgcn_readfirstlane(dst0 + kWaves * 1024 * k));
   };
   // Copies that fetch nothing needed: an in-bounds read of the pool's first rows
-  // into the spare kilobyte.  Every iteration issues the same number of copies,
-  // so one fixed wait count finds each stage landed.
+  // into a ring slot no later iteration of the range reads.  Every iteration
+  // issues the same number of copies, so one fixed wait count finds each stage
+  // landed.
   const uint64_t idle_base = uniform_addr(cache);
 
   int seg_i = wgseg[w];
@@ -286,10 +286,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
 
       // latent-product operands (stage it - 1), the first of them read during the score MFMAs
       const MLA_LDS uint8_t* pp = pbuf + ((it + 1) & 1) * kPBytes + lane * 16;
-      // A operand a = 4 hs + fb: feature block 4 wave + fb, token half hs; its two reads
+      // A operand ai = 4 hs + fb: feature block 4 wave + fb, token half hs; its two reads
       // take tokens 16 hs + 4 hh + e (r = 0) and 16 hs + 8 + 4 hh + e (r = 1)
-      auto rd = [&](int a) {
-        const int hs = a >> 2, FB = 4 * wave + (a & 3);
+      auto rd = [&](int ai) {
+        const int hs = ai >> 2, FB = 4 * wave + (ai & 3);
         const int o0 = (o_off[FB & 1] ^ (16 * (4 * hs))) + (FB >> 1) * 128 + (16 * hs) * (kRow * 2);
         const int o1 = (o_off[FB & 1] ^ (16 * (4 * hs + 2))) + (FB >> 1) * 128 + (16 * hs + 8) * (kRow * 2);
         const u32x2 lo2 = lds_read_tr16(sto + o0);

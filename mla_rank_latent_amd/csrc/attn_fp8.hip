@@ -391,9 +391,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
           }
         }
         const MLA_LDS uint8_t* pp = lds + kQP + ((it + 1) & 1) * kPBytes + lane * 16;
-        // A operand a = 4 hs + fb: feature block 4 wave + fb, token half hs
-        auto rd = [&](int a) {
-          const int hs = a >> 2, FB = 4 * wave + (a & 3);
+        // A operand ai = 4 hs + fb: feature block 4 wave + fb, token half hs
+        auto rd = [&](int ai) {
+          const int hs = ai >> 2, FB = 4 * wave + (ai & 3);
           const u32x2 raw = lds_read_tr8(sto + ((o8_off ^ (32 * (FB & 7))) + 256 * (FB >> 3) + hs * (16 * kLat)));
           const u32x2 c0 = cvt4(raw[0], 1.0f), c1 = cvt4(raw[1], 1.0f);
           return u32x4{c0[0], c0[1], c1[0], c1[1]};
