@@ -272,3 +272,30 @@ def test_append_many_tokens_bad_position_is_skipped():
     assert int(c.status.item()) & 0x4
     changed = np.any(after != before, axis=-1)
     assert changed.sum() == 2200 - 1
+
+
+@pytest.mark.parametrize("num_splits", [1, 7, 0])
+def test_weights_sum_to_one_through_the_whole_path(num_splits):
+    """Every cached latent's first feature set to 1 and every head's first W^UV row set to
+    e_0: the first output feature of every row is then sum_j p_j = 1, whatever the scores,
+    the paging, the split count and the merge.  The weights are rounded to bf16 once and the
+    weight sum adds the same rounded values; the partial latent sums carry one bf16 rounding
+    (at most 2^-9 relative), which the output's own rounding to bf16 absorbs, so the first
+    feature must come out within one bf16 step below 1."""
+    spec = H.small_spec("sum_one", 3, 2, [65, 700, 2049], seed=15)
+    x = synth.make_inputs(spec)
+    pool = x["pool"].copy()
+    pool[..., 0] = 0x3F80                                    # bf16 1.0
+    x["pool"] = pool
+    w_uv = synth.bf16_bits_to_f32(x["w_uv"]).copy()
+    rows0 = np.arange(spec.n_heads) * spec.d_nope            # row 0 of each head's W^UV_i
+    w_uv[rows0, :] = 0.0
+    w_uv[rows0, 0] = 1.0
+    x["w_uv"] = synth.f32_to_bf16_bits(w_uv.astype(np.float32))
+    import torch
+    c = H.GpuCase(x, num_splits)
+    c.decode()
+    torch.cuda.synchronize()
+    o0 = H.host(c.out)[..., 0].astype(np.float64)
+    H.log(f"  sum_one splits={num_splits}: first feature in [{o0.min():.6f}, {o0.max():.6f}]")
+    assert np.all(np.abs(o0 - 1.0) <= 2.0 ** -8), (o0.min(), o0.max())
