@@ -387,6 +387,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       }
     }
     const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0ull;
+    // The last two iterations' copies (idle ones, into ring slots (nsub + 1) & 3 and
+    // (nsub + 2) & 3) may still be in flight; they are asm, so the compiler does not wait
+    // for them.  The epilogue below reuses ring slots 0 and 1 and a retried range refills
+    // the ring, so every copy of this wave lands before the barrier.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();   // ring and weight slots free
     MLA_LDS int* flags = (MLA_LDS int*)pbuf;
     if (lane == 0) flags[wave] = wbad ? 1 : 0;

@@ -447,6 +447,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
       }
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0ull && lane == 0) s_retry = 1;
+    // every copy of this wave (asm, so not waited for by the compiler) lands before the
+    // epilogue or a retried range reuses the ring
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();   // ring free for the next range; every wave's flag visible
     const bool retry = s_retry != 0;
     __syncthreads();   // every wave has read the flag

@@ -139,12 +139,14 @@ def mla_layer_workspace_bytes(d: MlaDims, d_qlat: int, batch: int, sq: int) -> i
 def prepared_q_compress(d: MlaDims, d_qlat: int, h, w_dq, w_uq, w_qr, positions, q_nope, q_rope, workspace,
                         stream=None):
     """h [batch, sq, d_model] -> q_nope, q_rope (as mla_decode takes them) through the compressed query;
-    returns a zero-argument launcher (arguments marshalled once, return code checked on every call)."""
+    returns a zero-argument launcher (arguments marshalled once, return code checked on every call).  The
+    launcher keeps references to the tensors, so their memory stays valid while it lives."""
     batch, sq = int(h.shape[0]), int(h.shape[1])
+    keep = (d, h, w_dq, w_uq, w_qr, positions, q_nope, q_rope, workspace)
     args = (ctypes.byref(d), d_qlat, _ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(positions), _ptr(q_nope),
             _ptr(q_rope), batch, sq, _ptr(workspace), _nbytes(workspace), _stream(stream))
 
-    def launch() -> None:
+    def launch(_keep=keep) -> None:
         _check("mla_q_compress", _lib.mla_q_compress(*args))
     return launch
 
@@ -155,12 +157,14 @@ def mla_q_compress(d: MlaDims, d_qlat: int, h, w_dq, w_uq, w_qr, positions, q_no
 
 
 def prepared_out_project(d: MlaDims, o, w_o, u, workspace, stream=None):
-    """o [batch, sq, n_heads, d_nope] -> u [batch, sq, d_model]; returns a zero-argument launcher."""
+    """o [batch, sq, n_heads, d_nope] -> u [batch, sq, d_model]; returns a zero-argument launcher that
+    keeps references to the tensors."""
     batch, sq = int(o.shape[0]), int(o.shape[1])
+    keep = (d, o, w_o, u, workspace)
     args = (ctypes.byref(d), _ptr(o), _ptr(w_o), _ptr(u), batch, sq, _ptr(workspace), _nbytes(workspace),
             _stream(stream))
 
-    def launch() -> None:
+    def launch(_keep=keep) -> None:
         _check("mla_out_project", _lib.mla_out_project(*args))
     return launch
 
@@ -236,16 +240,18 @@ def mla_prefill(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_
 def prepared_prefill(fn_name: str, d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens,
                      softmax_scale: float, workspace, out, lse=None, status=None, stream=None):
     """Marshal the arguments of ``fn_name`` (mla_prefill or one of its phases, mla_prefill_expand and
-    mla_prefill_attend) once and return a zero-argument launcher; every launch still checks the return code."""
+    mla_prefill_attend) once and return a zero-argument launcher; every launch still checks the return code.
+    The launcher keeps references to the tensors, so their memory stays valid while it lives."""
     if fn_name not in ("mla_prefill", "mla_prefill_expand", "mla_prefill_attend"):
         raise ValueError(fn_name)
     batch, t = int(q_nope.shape[0]), int(q_nope.shape[1])
     fn = getattr(_lib, fn_name)
+    keep = (d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, workspace, out, lse, status)
     args = (ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
             _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, t, float(softmax_scale),
             _ptr(workspace), _nbytes(workspace), _ptr(out), _ptr(lse), _ptr(status), _stream(stream))
 
-    def launch() -> None:
+    def launch(_keep=keep) -> None:
         _check(fn_name, fn(*args))
     return launch
 

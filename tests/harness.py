@@ -45,14 +45,17 @@ def fp8_pages(pool_bits: np.ndarray, d_latent: int) -> np.ndarray:
     return mla_oracle.pack_fp8_pages(codes, pool_bits[..., d_latent:], scales)
 
 
-def with_fp8_cache(x: dict, pages: bool = True) -> dict:
+def with_fp8_cache(x: dict, pages: bool = False) -> dict:
     """A copy of generated inputs whose cache is FP8.  The oracle then reads every block as
-    its own quantisation of the bf16 block, dequantised; ``pages`` (what the GPU is handed)
-    is the oracle's quantisation of the whole pool."""
+    its own quantisation of the bf16 block, dequantised.  The GPU makes its pages from the
+    bf16 pool with the library's own quantiser (mla_cache_quantize), unless ``pages``: then
+    ``x["pages"]`` holds the oracle's quantisation of the whole pool and the GPU is handed
+    those bytes (for tests that craft or inspect page bytes)."""
     x8 = dict(x)
     x8["fp8"] = True
     if pages:
         x8["pages"] = fp8_pages(x["pool"], x["spec"].d_latent)
+        x8["pages_given"] = True
     return x8
 
 
@@ -79,7 +82,17 @@ class GpuCase:
         self.cache = cache
         self.d = mla_dims(spec, cache)
         self.num_splits = num_splits
-        self.pool = dev(x["pages"] if cache == "fp8" else x["pool"], spec.dtype)
+        if cache == "fp8" and not x.get("pages_given", False):
+            # the product chain: the library quantises the bf16 pool into its FP8 pages
+            from mla_rank_latent_amd import mla as _mla
+            src = dev(x["pool"], spec.dtype)
+            self.pool = torch.empty(int(x["pool"].shape[0]), _mla.MLA_FP8_PAGE_BYTES, dtype=torch.uint8,
+                                    device="cuda")
+            _mla.mla_cache_quantize(self.d, src, self.pool)
+            torch.cuda.synchronize()
+            del src
+        else:
+            self.pool = dev(x["pages"] if cache == "fp8" else x["pool"], spec.dtype)
         self.block_table = dev(x["block_table"], spec.dtype)
         self.seq_lens = dev(x["seq_lens"], spec.dtype)
         self.w_uk = dev(x["w_uk"], spec.dtype)
@@ -208,10 +221,11 @@ def oracle_append_rows(x: dict) -> np.ndarray:
                                  synth.as_float(x["w_kr"], spec.dtype), x["positions"], spec.rope_base, spec.dtype)
 
 
-def oracle_decode(x: dict, batches=None, heads=None, appended_rows=None, q=None):
+def oracle_decode(x: dict, batches=None, heads=None, appended_rows=None, q=None, heads_of=None):
     """Oracle output for the sampled sequences/heads.  ``appended_rows`` [B, T, R]
     are the oracle's own rows for the append positions (so the oracle never
-    reads a value the GPU wrote); ``q`` overrides (q_nope, q_rope) as float64."""
+    reads a value the GPU wrote); ``q`` overrides (q_nope, q_rope) as float64;
+    ``heads_of(b)``, if given, names the heads evaluated for sequence b."""
     spec = x["spec"]
     B, bs = spec.batch, spec.block_size
     batches = list(range(B)) if batches is None else list(batches)
@@ -230,9 +244,30 @@ def oracle_decode(x: dict, batches=None, heads=None, appended_rows=None, q=None)
             for t, p in enumerate(x["positions"][b]):
                 sub[p // bs, p % bs] = appended_rows[b, t]
         o, l = mla_oracle.decode(qn[b:b + 1], qr[b:b + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :], [L],
-                                 x["scale"], bs, heads=heads)
+                                 x["scale"], bs, heads=heads if heads_of is None else heads_of(b))
         out[b], lse[b] = o[0], l[0]
     return out, lse
+
+
+def oracle_single_queries(x: dict, b: int, queries):
+    """Oracle out [len(queries), H, d_h] and lse [len(queries), H] for chosen queries s of
+    sequence b's group, every head: query s is a single query over the first
+    L - Sq + s + 1 tokens (the causal rule of a query group)."""
+    spec = x["spec"]
+    bs = spec.block_size
+    qn, qr = synth.as_float(x["q_nope"][b], spec.dtype), synth.as_float(x["q_rope"][b], spec.dtype)
+    w_uk, w_uv = synth.as_float(x["w_uk"], spec.dtype), synth.as_float(x["w_uv"], spec.dtype)
+    L = int(x["seq_lens"][b])
+    nblk = (L + bs - 1) // bs
+    sub = pool_blocks(x, x["block_table"][b, :nblk])
+    outs, lses = [], []
+    for s in queries:
+        n = L - spec.sq + int(s) + 1
+        o, l = mla_oracle.decode(qn[None, s:s + 1], qr[None, s:s + 1], w_uk, w_uv, sub, np.arange(nblk)[None, :],
+                                 [n], x["scale"], bs)
+        outs.append(o[0, 0])
+        lses.append(l[0, 0])
+    return np.stack(outs), np.stack(lses)
 
 
 def oracle_query_samples(x: dict, samples):

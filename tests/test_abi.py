@@ -294,3 +294,38 @@ def test_fp8_cache_entry_points_on_the_host():
     assert mla.mla_prefill_workspace_bytes(f8, 2, 4) == 0
     # the layer's projections take its bf16 tensors
     assert mla.mla_layer_workspace_bytes(f8, 1536, 64, 1) == mla.mla_layer_workspace_bytes(v2, 1536, 64, 1)
+
+
+def test_prepared_launchers_keep_their_tensors_alive():
+    """Every prepared launcher holds the tensors whose addresses it marshalled: a caller that
+    drops its own references must not leave the launcher with freed memory.  The tensors
+    are released once the launcher itself goes."""
+    import gc
+    import weakref
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    T = _FakeTensor
+
+    def tensors(n):
+        return [T(FAKE + 256 * i, (2, 1, 128, 128)) for i in range(n)]
+
+    makers = {
+        "q_compress": (8, lambda t: mla.prepared_q_compress(v2, 1536, t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7],
+                                                            stream=0)),
+        "out_project": (4, lambda t: mla.prepared_out_project(v2, t[0], t[1], t[2], t[3], stream=0)),
+        "prefill": (10, lambda t: mla.prepared_prefill("mla_prefill", v2, t[0], t[1], t[2], t[3], t[4], t[5], t[6],
+                                                       0.07, t[7], t[8], lse=t[9], stream=0)),
+        "cache_append": (7, lambda t: mla.prepared_cache_append(v2, t[0], t[1], t[2], t[3], t[4], t[5], t[6],
+                                                                stream=0)),
+        "decode": (10, lambda t: mla.prepared_decode("mla_decode", v2, t[0], t[1], t[2], t[3], t[4], t[5], t[6],
+                                                     0.07, t[7], t[8], lse=t[9], stream=0)),
+    }
+    for name, (n, make) in makers.items():
+        ts = tensors(n)
+        refs = [weakref.ref(t) for t in ts]
+        launch = make(ts)
+        del ts
+        gc.collect()
+        assert all(r() is not None for r in refs), name
+        del launch
+        gc.collect()
+        assert all(r() is None for r in refs), name
