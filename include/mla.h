@@ -30,9 +30,11 @@
  *    its table row) are never turned into out-of-bounds accesses: the access
  *    is clamped or skipped and the matching MLA_STATUS_* bit is OR-ed into
  *    the optional device word `status`.
- *  - The library's only mutable global state is a per-device cache of the
- *    compute-unit count (written once, atomically); concurrent calls on different
- *    streams are safe as long as they do not share output or workspace memory.
+ *  - The library's mutable global state is a per-device cache of the compute-unit
+ *    count and of the scratch array's address (each written once, atomically), and
+ *    that scratch array itself, which only mla_decode_noalloc uses; concurrent calls
+ *    on different streams are safe as long as they do not share output or workspace
+ *    memory (mla_decode_noalloc: see there).
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -54,6 +56,7 @@ extern "C" {
 #define MLA_ERR_CAPACITY             -6  /* a size exceeds what the kernels index (see below) */
 #define MLA_ERR_HIP                  -7  /* the HIP runtime refused a launch */
 #define MLA_ERR_UNSUPPORTED          -8  /* valid dims or dtype this entry point is not built for */
+#define MLA_ERR_SCRATCH_TOO_SMALL    -9  /* mla_decode_noalloc: the shape needs more than its scratch */
 
 /* bits OR-ed into *status by the kernels */
 #define MLA_STATUS_BAD_BLOCK   0x1  /* block_table named a block outside [0, num_blocks) */
@@ -272,6 +275,30 @@ int mla_decode_finish(const mla_dims* dims, const void* q_nope, const void* q_ro
                       int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
                       void* workspace, size_t workspace_bytes, void* out, float* lse,
                       int32_t* status, void* stream);
+
+/*
+ * mla_decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks, results and conventions as mla_decode with
+ * the same num_splits, minus workspace and workspace_bytes: the workspace is a
+ * static device array of MLA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the first call on that GPU until the process ends (the first call on a
+ * device looks up its address; no call allocates or frees anything).
+ *  - A shape whose mla_decode_workspace_bytes(dims, batch, sq, num_splits) exceeds
+ *    MLA_NOALLOC_SCRATCH_BYTES returns MLA_ERR_SCRATCH_TOO_SMALL before anything is
+ *    launched (64 MiB holds batch 64 x 128 heads at one query token, the decode
+ *    benchmark's shape, with room to spare; use mla_decode for larger shapes).
+ *  - Every call on one GPU uses that GPU's one array, and nothing in it has to start
+ *    at any value (each call writes what it reads).  Calls that overlap in time on
+ *    one GPU (other streams, other host threads) race on it and give wrong results:
+ *    order them on one stream, or use mla_decode with separate workspaces.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int mla_decode_noalloc(const mla_dims* dims, const void* q_nope, const void* q_rope,
+                       const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks,
+                       const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                       int32_t batch, int32_t sq, float softmax_scale, int32_t num_splits,
+                       void* out, float* lse, int32_t* status, void* stream);
 
 /*
  * The full layer's projections around attention ("DeepSeek-V2 ... MLA" page

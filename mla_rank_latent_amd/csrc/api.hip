@@ -4,8 +4,14 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "mla_internal.h"
+
+// Device scratch of mla_decode_noalloc, for callers that cannot allocate: one copy per GPU,
+// held until the process ends.  In host code this name is only a stand-in for the symbol;
+// the device address comes from hipGetSymbolAddress (noalloc_scratch() below).
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace mla {
 
@@ -144,6 +150,8 @@ const char* mla_status_str(int code) {
     case MLA_ERR_CAPACITY: return "a size exceeds what the kernels can index";
     case MLA_ERR_HIP: return "the HIP runtime refused a launch";
     case MLA_ERR_UNSUPPORTED: return "dims or an element type this entry point is not built for";
+    case MLA_ERR_SCRATCH_TOO_SMALL:
+      return "the shape needs more than the MLA_NOALLOC_SCRATCH_BYTES of scratch mla_decode_noalloc holds";
     default: return "unknown status code";
   }
 }
@@ -154,6 +162,8 @@ size_t mla_cache_bytes(const mla_dims* dims, int64_t tokens) {
   return (size_t)tokens * ((size_t)dims->d_latent + dims->d_rope) * elem_size(dims->dtype);
 }
 
+}  // extern "C"
+
 namespace {
 bool append_uses_gemm(const mla_dims* d, long long tokens) {
   return is_bf(d) && tokens >= kAppendGemmMinTokens && d->d_model % 64 == 0;
@@ -162,6 +172,8 @@ bool append_uses_gemm(const mla_dims* d, long long tokens) {
 // their pages; the split path's partial products follow the staging rows
 size_t fp8_staging_bytes(long long tokens) { return up((size_t)tokens * kRow * 2); }
 }  // namespace
+
+extern "C" {
 
 size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t t) {
   if (check_dims(dims) != MLA_OK || batch < 1 || t < 1 || (long long)batch * t >= (1ll << 30)) return 0;
@@ -240,6 +252,8 @@ int mla_cache_quantize(const mla_dims* dims, const void* src, void* pages, int32
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+}  // extern "C"
+
 namespace {
 // the full layer's projections run on bf16 tiles of 64 features (d_qlat 0: not used by the call)
 int check_layer(const mla_dims* d, int d_qlat, int batch, int sq) {
@@ -260,6 +274,8 @@ size_t q_compress_bytes(const mla_dims* d, int d_qlat, int M) {
   return cq + up(part);
 }
 }  // namespace
+
+extern "C" {
 
 size_t mla_layer_workspace_bytes(const mla_dims* dims, int32_t d_qlat, int32_t batch, int32_t sq) {
   if (check_layer(dims, d_qlat, batch, sq) != MLA_OK) return 0;
@@ -333,29 +349,59 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s
   return L.total;
 }
 
+}  // extern "C"
+
 namespace {
 
 constexpr int kPhasePrepare = 1, kPhaseAttend = 2, kPhaseFinish = 4;
 
-int decode_phases(int phases, const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
-                  const void* w_uv, const void* cache, int32_t num_blocks, const int32_t* block_table,
-                  int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t sq, float softmax_scale,
-                  int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, float* lse, int32_t* status,
-                  void* stream) {
+// The scratch array's device address on the current device, looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept.
+std::atomic<void*> g_scratch[64];
+std::mutex g_scratch_mu;
+
+int noalloc_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLA_ERR_HIP;
+  if (dev >= 64) return MLA_ERR_CAPACITY;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MLA_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return MLA_OK;
+}
+
+// use_scratch: the phases run in this device's scratch array (mla_decode_noalloc), and
+// workspace / workspace_bytes are ignored
+int decode_impl(int phases, bool use_scratch, const mla_dims* dims, const void* q_nope, const void* q_rope,
+                const void* w_uk, const void* w_uv, const void* cache, int32_t num_blocks, const int32_t* block_table,
+                int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t sq, float softmax_scale,
+                int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, float* lse, int32_t* status,
+                void* stream) {
   int rc = check_dims(dims);
   if (rc != MLA_OK) return rc;
-  if (!q_nope || !w_uk || !w_uv || !cache || !block_table || !seq_lens || !workspace || !out) return MLA_ERR_NULL_PTR;
+  if (use_scratch) workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  if (!q_nope || !w_uk || !w_uv || !cache || !block_table || !seq_lens || (!workspace && !use_scratch) || !out)
+    return MLA_ERR_NULL_PTR;
   if (dims->d_rope > 0 && !q_rope) return MLA_ERR_NULL_PTR;
   if ((rc = check_sq(dims, sq)) != MLA_OK) return rc;
   if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
   if (num_splits < 0 || !std::isfinite(softmax_scale)) return MLA_ERR_BAD_DIMS;
   if (!aligned16(q_nope) || (q_rope && !aligned16(q_rope)) || !aligned16(w_uk) || !aligned16(w_uv) ||
       !aligned16(cache) || !aligned16(block_table) || !aligned16(seq_lens) || !aligned16(out) ||
-      ((uintptr_t)workspace & (kAlign - 1)) || (lse && ((uintptr_t)lse & 3u)) || (status && ((uintptr_t)status & 3u)))
+      (!use_scratch && ((uintptr_t)workspace & (kAlign - 1))) || (lse && ((uintptr_t)lse & 3u)) ||
+      (status && ((uintptr_t)status & 3u)))
     return MLA_ERR_BAD_ALIGN;
   WsLayout L;
   if (!ws_layout(dims, batch, sq, num_splits, &L)) return MLA_ERR_HIP;
-  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < L.total) return use_scratch ? MLA_ERR_SCRATCH_TOO_SMALL : MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (use_scratch && (rc = noalloc_scratch(&workspace)) != MLA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   hipError_t e = hipSuccess;
@@ -382,6 +428,8 @@ int decode_phases(int phases, const mla_dims* dims, const void* q_nope, const vo
 
 }  // namespace
 
+extern "C" {
+
 #define MLA_DECODE_ARGS                                                                                          \
   dims, q_nope, q_rope, w_uk, w_uv, cache, num_blocks, block_table, max_blocks, seq_lens, batch, sq, softmax_scale, \
       num_splits, workspace, workspace_bytes, out, lse, status, stream
@@ -392,11 +440,20 @@ int decode_phases(int phases, const mla_dims* dims, const void* q_nope, const vo
       size_t workspace_bytes, void *out, float *lse, int32_t *status, void *stream
 
 int mla_decode(MLA_DECODE_PARAMS) {
-  return decode_phases(kPhasePrepare | kPhaseAttend | kPhaseFinish, MLA_DECODE_ARGS);
+  return decode_impl(kPhasePrepare | kPhaseAttend | kPhaseFinish, false, MLA_DECODE_ARGS);
 }
-int mla_decode_prepare(MLA_DECODE_PARAMS) { return decode_phases(kPhasePrepare, MLA_DECODE_ARGS); }
-int mla_decode_attend(MLA_DECODE_PARAMS) { return decode_phases(kPhaseAttend, MLA_DECODE_ARGS); }
-int mla_decode_finish(MLA_DECODE_PARAMS) { return decode_phases(kPhaseFinish, MLA_DECODE_ARGS); }
+int mla_decode_prepare(MLA_DECODE_PARAMS) { return decode_impl(kPhasePrepare, false, MLA_DECODE_ARGS); }
+int mla_decode_attend(MLA_DECODE_PARAMS) { return decode_impl(kPhaseAttend, false, MLA_DECODE_ARGS); }
+int mla_decode_finish(MLA_DECODE_PARAMS) { return decode_impl(kPhaseFinish, false, MLA_DECODE_ARGS); }
+
+int mla_decode_noalloc(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
+                       const void* w_uv, const void* cache, int32_t num_blocks, const int32_t* block_table,
+                       int32_t max_blocks, const int32_t* seq_lens, int32_t batch, int32_t sq, float softmax_scale,
+                       int32_t num_splits, void* out, float* lse, int32_t* status, void* stream) {
+  return decode_impl(kPhasePrepare | kPhaseAttend | kPhaseFinish, true, dims, q_nope, q_rope, w_uk, w_uv, cache,
+                     num_blocks, block_table, max_blocks, seq_lens, batch, sq, softmax_scale, num_splits, nullptr,
+                     0, out, lse, status, stream);
+}
 
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_blocks) {
   if (check_dims(dims) != MLA_OK || dims->dtype != MLA_DTYPE_BF16 || batch < 1 || batch > 65536 || max_blocks < 1 ||

@@ -28,7 +28,9 @@ EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_a
            "mla_cache_quantize",
            "mla_q_project", "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
            "mla_decode_finish", "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_expand",
-           "mla_prefill_attend", "mla_layer_workspace_bytes", "mla_q_compress", "mla_out_project")
+           "mla_prefill_attend", "mla_layer_workspace_bytes", "mla_q_compress", "mla_out_project",
+           "mla_decode_noalloc")
+MLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (or python -m mla_rank_latent_amd.build)")
@@ -86,6 +88,9 @@ for _name in ("mla_decode", "mla_decode_prepare", "mla_decode_attend", "mla_deco
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
                                      ctypes.c_float, _I, _P, ctypes.c_size_t, _P, _P, _P, _P]
+_lib.mla_decode_noalloc.restype = ctypes.c_int
+_lib.mla_decode_noalloc.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
+                                    ctypes.c_float, _I, _P, _P, _P, _P]
 
 
 class MlaError(RuntimeError):
@@ -225,6 +230,17 @@ def mla_decode(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_l
     ``workspace`` is a byte tensor of at least mla_decode_workspace_bytes(d, batch, sq, num_splits)."""
     _decode_call("mla_decode", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
                  workspace, out, lse, status, num_splits, stream)
+
+
+def mla_decode_noalloc(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,
+                       out, lse=None, status=None, num_splits: int = 0, stream=None) -> None:
+    """mla_decode without a workspace argument: the library's own per-GPU scratch array is used
+    (shapes up to MLA_NOALLOC_SCRATCH_BYTES of workspace; calls that overlap on one GPU race)."""
+    batch, sq = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _check("mla_decode_noalloc", _lib.mla_decode_noalloc(
+        ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache), int(cache.shape[0]),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), batch, sq, float(softmax_scale), num_splits,
+        _ptr(out), _ptr(lse), _ptr(status), _stream(stream)))
 
 
 def mla_prefill(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,

@@ -36,7 +36,7 @@ def test_one_hip_runtime_whatever_the_import_order():
 
 
 def test_status_strings():
-    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8]
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8, -9]
     strs = [mla.mla_status_str(c) for c in codes]
     assert len(set(strs)) == len(codes)
     assert mla.mla_status_str(-99) == "unknown status code"
@@ -329,3 +329,24 @@ def test_prepared_launchers_keep_their_tensors_alive():
         del launch
         gc.collect()
         assert all(r() is None for r in refs), name
+
+
+def test_noalloc_decode_rejects_before_any_device_call():
+    """mla_decode_noalloc checks its arguments, and that the shape's workspace fits its scratch
+    array, on the host before it touches a device (these calls run without a GPU)."""
+    lib = mla.raw_library()
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+
+    def call(batch, sq, num_splits, q=FAKE, out=FAKE):
+        return lib.mla_decode_noalloc(ctypes.byref(v2), q, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 16, FAKE, batch, sq,
+                                      0.07, num_splits, out, None, None, None)
+
+    assert call(4, 1, 8, q=None) == -1
+    assert call(4, 1, 8, out=None) == -1
+    assert call(4, 9, 8) == -6                     # more query tokens than the kernels take
+    need = mla.mla_decode_workspace_bytes(v2, 4096, 1, 64)
+    assert need > mla.MLA_NOALLOC_SCRATCH_BYTES
+    assert call(4096, 1, 64) == -9                 # its workspace would not fit the scratch array
+    assert "scratch" in mla.mla_status_str(-9)
+    # the decode benchmark's shape fits (batch 64, 128 heads, one query token, 256 ranges)
+    assert mla.mla_decode_workspace_bytes(v2, 64, 1, 256) <= mla.MLA_NOALLOC_SCRATCH_BYTES
