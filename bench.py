@@ -38,33 +38,86 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 FP8_SUFFIX = "_fp8"   # a decode workload with its cache in FP8 pages
 _COMMON_SOURCES = ("mla_rank_latent_amd/csrc/attn_common.h", "mla_rank_latent_amd/csrc/device_util.h",
                    "mla_rank_latent_amd/csrc/mla_internal.h")
-# the counter profile of each decode workload's attention kernel, and the sources it was taken from
-TRAFFIC_PROFILES = {
-    "v2_b64_ctx8192_paged_append": ("attn_bf16_b64_ctx8192_hbm_traffic.md",
-                                    ("mla_rank_latent_amd/csrc/attn_bf16.hip",) + _COMMON_SOURCES),
-    "v2_b64_ctx8192_paged_append_fp8": ("attn_fp8_b64_ctx8192_hbm_traffic.md",
+# The counter profile of each decode workload's attention kernel (HBM traffic from FETCH_SIZE and
+# WRITE_SIZE, MFMA busy cycles), and the sources it was taken from.
+_BF16_SOURCES = ("mla_rank_latent_amd/csrc/attn_bf16.hip",) + _COMMON_SOURCES
+COUNTER_PROFILES = {
+    "v2_b64_ctx8192_paged_append": ("attn_bf16_b64_ctx8192_counters.md", _BF16_SOURCES),
+    "v2_b1_ctx4096": ("attn_bf16_b1_ctx4096_counters.md", _BF16_SOURCES),
+    "v2_b4_longctx_128k": ("attn_bf16_b4_longctx_counters.md", _BF16_SOURCES),
+    "v2_b128_ragged_sq2": ("attn_bf16_b128_ragged_sq2_counters.md", _BF16_SOURCES),
+    "v2_b64_ctx8192_paged_append_fp8": ("attn_fp8_b64_ctx8192_counters.md",
                                         ("mla_rank_latent_amd/csrc/attn_fp8.hip",) + _COMMON_SOURCES),
 }
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter profile, or None when there is none for
-    this workload or the attention sources changed since the counters were taken."""
-    if workload not in TRAFFIC_PROFILES:
-        return None
-    name, sources = TRAFFIC_PROFILES[workload]
-    try:
-        text = open(os.path.join(ROOT, "profiles", name), encoding="utf-8").read()
-    except OSError:
-        return None
-    fields = dict(re.findall(r"^- ([a-z0-9_]+): (\S+)$", text, flags=re.M))
+def sources_sha256(sources) -> str:
     h = hashlib.sha256()
     for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    if fields.get("workload") != workload or fields.get("attention_sources_sha256") != h.hexdigest():
-        return None
-    return int(fields["traffic_bytes_per_launch"])
+    return h.hexdigest()
+
+
+def measured_counters(workload: str) -> dict:
+    """Figures per attention launch from the committed counter profile of this workload:
+    ``traffic`` (HBM bytes, FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's reading) and
+    ``mfma_busy`` (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 4 SIMDs x CUs).  Empty when
+    there is no profile or the attention sources changed since the counters were taken."""
+    if workload not in COUNTER_PROFILES:
+        return {}
+    name, sources = COUNTER_PROFILES[workload]
+    try:
+        text = open(os.path.join(ROOT, "profiles", name), encoding="utf-8").read()
+    except OSError:
+        return {}
+    fields = dict(re.findall(r"^- ([a-z0-9_]+): (\S+)$", text, flags=re.M))
+    if fields.get("workload") != workload or fields.get("attention_sources_sha256") != sources_sha256(sources):
+        return {}
+    out = {}
+    if "traffic_bytes_per_launch" in fields:
+        out["traffic"] = int(fields["traffic_bytes_per_launch"])
+    if "mfma_busy_frac" in fields:
+        out["mfma_busy"] = float(fields["mfma_busy_frac"])
+    return out
+
+
+def host_info() -> dict:
+    """The host's CPU model, numpy's BLAS backend and the threads it uses."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count() or 1
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(i.get("num_threads", 1) for i in info)
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "threads": int(threads)}
+
+
+MALL_BYTES = 256 * 1024 * 1024   # MI355X last-level (Infinity) cache
+
+
+def rotation_copies(rotate: int, step_bytes: int) -> int:
+    """Input copies a timed run cycles through.  rotate > 0: that many.  0 (auto): enough that
+    between two uses of one copy the other copies move at least twice the last-level cache,
+    so no step finds what it reads still cached from an earlier step."""
+    if rotate > 0:
+        return rotate
+    k = 1
+    while (k - 1) * step_bytes < 2 * MALL_BYTES:
+        k += 1
+    return max(k, 2)
 
 
 def workload_bytes_flops(spec, seq_lens, fp8: bool = False):
@@ -122,11 +175,8 @@ def cpu_baseline_prefill(x, budget_s: float):
     import numpy as np
     from mla_rank_latent_amd import synth
     from oracle import mla_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    hi = host_info()
+    threads = hi["threads"]
     spec = x["spec"]
     bs = spec.block_size
     L = int(x["seq_lens"][0])
@@ -151,6 +201,7 @@ def cpu_baseline_prefill(x, budget_s: float):
     f = prefill_flops(spec, x["seq_lens"][:1])
     done = f["append"] / spec.batch + (f["expand"] + f["attn"]) / spec.batch * heads / spec.n_heads
     return {"value": round(done / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": hi["cpu_model"], "blas": hi["blas"],
             "sample": f"sequence 0: its {spec.sq} appended rows and {heads} of {spec.n_heads} heads (every query) "
                       f"in {spent:.1f} s; fp64 numpy; TFLOP/s of the same algorithmic flops"}
 
@@ -364,7 +415,7 @@ def run_layer(args, spec, x) -> int:
         "step_bytes": step_bytes,
         "step_flops": step_flops,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(spec.name),
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
                      "bytes_per_launch": wl["cache_bytes"], "mfma_tflops": round(attn_tflops, 2)},
         "cpu_baseline": None,
@@ -383,11 +434,8 @@ def cpu_baseline_layer(x, budget_s: float, step_bytes: int):
     import numpy as np
     from mla_rank_latent_amd import synth
     from oracle import mla_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    hi = host_info()
+    threads = hi["threads"]
     spec = x["spec"]
     bs = spec.block_size
     f = lambda k: synth.as_float(x[k], spec.dtype)
@@ -413,6 +461,7 @@ def cpu_baseline_layer(x, budget_s: float, step_bytes: int):
             break
     value = step_bytes * done / spec.batch / spent / 1e9
     return {"value": round(value, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": hi["cpu_model"], "blas": hi["blas"],
             "sample": f"{done} of {spec.batch} sequences (append, compressed queries, all {spec.n_heads} heads, "
                       f"W^O) in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
 
@@ -425,11 +474,8 @@ def cpu_baseline(x, budget_s: float, fp8: bool = False):
     import numpy as np
     from mla_rank_latent_amd import synth
     from oracle import mla_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    hi = host_info()
+    threads = hi["threads"]
     spec = x["spec"]
     bs = spec.block_size
     qn, qr = synth.as_float(x["q_nope"], spec.dtype), synth.as_float(x["q_rope"], spec.dtype)
@@ -461,6 +507,7 @@ def cpu_baseline(x, budget_s: float, fp8: bool = False):
     value = wb * done / spec.batch / spent / 1e9
     what = ", FP8 quantise/dequantise included" if fp8 else ""
     return {"value": round(value, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": hi["cpu_model"], "blas": hi["blas"],
             "sample": f"{done} of {spec.batch} sequences (all {spec.n_heads} heads, full context, append included"
                       f"{what}) in {spent:.1f} s; fp64 numpy, non-absorbed; GB/s of the same algorithmic bytes"}
 
@@ -472,6 +519,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="v2_b64_ctx8192_paged_append")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies cycled through by the steps (0: enough that every step reads cold inputs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -518,47 +567,66 @@ def main() -> int:
 
     d = mla.dims(spec.n_heads, spec.d_nope, spec.d_rope, spec.d_latent, spec.d_model, spec.block_size,
                  "bf16_fp8" if fp8 else spec.dtype, spec.rope_base)
-    pool, bt, lens = dev(x["pool"]), dev(x["block_table"]), dev(x["seq_lens"])
-    if fp8:
-        # the cache in FP8 pages, quantised on the GPU from the generated bf16 cache
-        pages = torch.empty(pool.shape[0], mla.MLA_FP8_PAGE_BYTES, dtype=torch.uint8, device="cuda")
-        mla.mla_cache_quantize(d, pool, pages)
-        torch.cuda.synchronize()
-        pool = pages
-    w_uk, w_uv = dev(x["w_uk"]), dev(x["w_uv"])
-    qn, qr = dev(x["q_nope"]), dev(x["q_rope"])
-    has_append = spec.append
-    if has_append:
-        h, w_dkv, w_kr, pos = dev(x["h"]), dev(x["w_dkv"]), dev(x["w_kr"]), dev(x["positions"])
+    wl = workload_bytes_flops(spec, x["seq_lens"], fp8)
+    copies = rotation_copies(args.rotate, wl["bytes"])
+    print(f"[bench] {copies} input copies in rotation ({wl['bytes'] / 1e6:.1f} MB read per step)", file=sys.stderr,
+          flush=True)
+    bt, lens = dev(x["block_table"]), dev(x["seq_lens"])
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     out = torch.empty(spec.batch, spec.sq, spec.n_heads, spec.d_nope, dtype=tdt, device="cuda")
     lse = torch.empty(spec.batch, spec.sq, spec.n_heads, dtype=torch.float32, device="cuda")
     ws = torch.empty(mla.mla_decode_workspace_bytes(d, spec.batch, spec.sq, args.num_splits), dtype=torch.uint8,
                      device="cuda")
     stream = torch.cuda.current_stream()
-    dec_args = (d, qn, qr, w_uk, w_uv, pool, bt, lens, x["scale"], ws, out)
-
-    # arguments marshalled once, so that a step costs the host four foreign calls
-    launches = []
+    has_append = spec.append
+    append_ws = None
     if has_append:
-        n_ws = mla.mla_cache_append_workspace_bytes(d, int(h.shape[0]), int(h.shape[1]))
+        n_ws = mla.mla_cache_append_workspace_bytes(d, spec.batch, spec.sq)
         append_ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws else None
-        launches.append(mla.prepared_cache_append(d, h, w_dkv, w_kr, pos, bt, pool, workspace=append_ws,
-                                                  stream=stream))
-    phase = {name: mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits, stream=stream)
-             for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish")}
+        pos = dev(x["positions"])
+
+    # Every copy holds its own cache, queries, weights and hidden states (each step reads one
+    # copy, so nothing a step reads is still in the caches from the step before); arguments are
+    # marshalled once per copy, so a step costs the host four foreign calls.
+    sets = []
+    base = None
+    for k in range(copies):
+        if k == 0:
+            pool = dev(x["pool"])
+            if fp8:
+                # the cache in FP8 pages, quantised on the GPU from the generated bf16 cache
+                pages = torch.empty(pool.shape[0], mla.MLA_FP8_PAGE_BYTES, dtype=torch.uint8, device="cuda")
+                mla.mla_cache_quantize(d, pool, pages)
+                torch.cuda.synchronize()
+                pool = pages
+            t = dict(pool=pool, w_uk=dev(x["w_uk"]), w_uv=dev(x["w_uv"]), qn=dev(x["q_nope"]), qr=dev(x["q_rope"]))
+            if has_append:
+                t.update(h=dev(x["h"]), w_dkv=dev(x["w_dkv"]), w_kr=dev(x["w_kr"]))
+            base = t
+        else:
+            t = {key: v.clone() for key, v in base.items()}
+        launches = []
+        if has_append:
+            launches.append(mla.prepared_cache_append(d, t["h"], t["w_dkv"], t["w_kr"], pos, bt, t["pool"],
+                                                      workspace=append_ws, stream=stream))
+        dec_args = (d, t["qn"], t["qr"], t["w_uk"], t["w_uv"], t["pool"], bt, lens, x["scale"], ws, out)
+        for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
+            launches.append(mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits, stream=stream))
+        sets.append(launches)
+    torch.cuda.synchronize()
+    counter = [0]
 
     def step(ev_a=None, ev_b=None):
-        for launch in launches:
+        launches = sets[counter[0] % copies]
+        counter[0] += 1
+        for launch in launches[:-2]:      # append (if any), then prepare
             launch()
-        phase["mla_decode_prepare"]()
         if ev_a is not None:
             ev_a.record(stream)
-        phase["mla_decode_attend"]()
+        launches[-2]()                    # attend
         if ev_b is not None:
             ev_b.record(stream)
-        phase["mla_decode_finish"]()
-
+        launches[-1]()                    # finish
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -584,7 +652,6 @@ def main() -> int:
           f"attention {ms_attn * 1e3:.1f} us; host issue {enqueued / args.steps * 1e6:.1f} us/step", file=sys.stderr,
           flush=True)
 
-    wl = workload_bytes_flops(spec, x["seq_lens"], fp8)
     step_s = ms_step * 1e-3
     gbs = wl["bytes"] / step_s / 1e9
     tflops = wl["flops"] / step_s / 1e12
@@ -592,6 +659,27 @@ def main() -> int:
     attn_gbs = wl["cache_bytes"] / (ms_attn * 1e-3) / 1e9
     attn_tflops = wl["attn_flops"] / (ms_attn * 1e-3) / 1e12
 
+    # The attention kernel's bound: HBM while its arithmetic intensity (flops per cache byte) is
+    # under the chip's ridge point (2.5 PFLOP/s over 8 TB/s = 312.5 flop/B, one query token per
+    # sequence), the bf16 MFMA peak above it (two or more query tokens per sequence).
+    counters = measured_counters(args.workload)
+    kernel_s = ms_attn * 1e-3
+    mfma_bound = wl["attn_flops"] / wl["cache_bytes"] > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": counters.get("traffic"), "flops_per_launch": wl["attn_flops"],
+                    "hbm_gbs": round(attn_gbs, 2), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": counters.get("traffic"),
+                    "bytes_per_launch": wl["cache_bytes"], "mfma_tflops": round(attn_tflops, 2),
+                    "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roofline.update({"kernel": "attn_fp8_kernel" if fp8 else "attn_bf16_kernel",
+                     "kernel_us": round(kernel_s * 1e6, 2),
+                     # counter-based share of the matrix cores' cycles spent busy, from the
+                     # committed rocprofv3 profile of this kernel (null if the sources changed)
+                     "mfma_busy_counter": counters.get("mfma_busy")})
     res = {
         "metric": "MLA decode GB/s + TFLOP/s (% roofline), tokens/s; B=64 ctx=8K 128 heads",
         "value": round(gbs, 2),
@@ -617,12 +705,7 @@ def main() -> int:
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "step_bytes": wl["bytes"],
         "step_flops": wl["flops"],
-        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-                     "kernel": "attn_fp8_kernel" if fp8 else "attn_bf16_kernel", "kernel_us": round(ms_attn * 1e3, 2),
-                     "bytes_per_launch": wl["cache_bytes"],
-                     "mfma_tflops": round(attn_tflops, 2),
-                     "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
