@@ -28,7 +28,12 @@
 // drop to a quarter.  The cache tile is read from HBM once per workgroup.
 //  - Software pipeline: iteration it scores stage it, then runs the latent
 //    product of stage it - 1 with stage it's softmax interleaved between its
-//    MFMAs step by step (the exponentials spread over the whole product).
+//    MFMAs step by step (one exponential per MFMA).  The product's last four
+//    MFMAs run after the next iteration's barrier, from operands kept in
+//    registers, while that iteration's first score operands are read; the next
+//    product's first operands are read during the score chain; and the chain's
+//    result is first read four product MFMAs after its last MFMA, so the matrix
+//    core waits on neither LDS latency nor a result hazard at either phase edge.
 //    The score accumulators live in VGPRs (the score MFMAs are issued as asm
 //    in their VGPR form), the latent accumulators in AGPRs, so no accumulator
 //    is ever moved between the two register files.
@@ -66,11 +71,24 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 static_assert(kWaves * kRowsPerWave == kRowsWG, "rows per workgroup");
 constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;   // 9 copies of 1 KB per wave and stage
-constexpr int kPfS = 4;   // score operands read ahead
+constexpr int kPfS = 3;   // score operands read ahead (measured: 3 beats 2 and 4)
 constexpr int kPBytes = kRowsWG * kSubTok * 2;   // one stage's weights for all rows: 8 KB
 
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};   // weight sum as a packed dot product
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
+
+// Maxima of scores: -inf (masked) and finite values only, so the canonicalising moves
+// the compiler adds around fmaxf are not needed.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 }  // namespace
 
@@ -258,7 +276,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
 
     // Iteration it scores stage it and, interleaved with that stage's softmax,
     // runs the latent product of stage it - 1, so the softmax's vector work
-    // overlaps matrix work.  Iteration nsub only finishes the last product.
+    // overlaps matrix work.  Iteration nsub only finishes the last product.  The
+    // product's last four MFMAs (token half 1, feature block 3, the four row blocks)
+    // run at the start of the next iteration, right after its barrier, from operands
+    // kept in registers: that matrix work covers the latency of the first score-operand
+    // reads.  Before the first iteration the kept operands are zero (0 x 0 is added).
+    u32x4 tail_a = u32x4{0u, 0u, 0u, 0u};
+    u32x4 tail_b[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) tail_b[rb] = u32x4{0u, 0u, 0u, 0u};
     for (int it = 0; it <= nsub; ++it) {
       // This wave's copies of stage it have landed once at most one stage's worth
       // (issued by the previous iteration) remains in flight.
@@ -305,6 +331,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
         u32x4 tv[kPfS];
 #pragma unroll
         for (int k = 0; k < kPfS; ++k) tv[k] = lds_read16(st + s_off[k & 3] + (k >> 2) * 128);
+        __builtin_amdgcn_sched_barrier(0);
+        // the previous product's last four MFMAs while the first reads land
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          acc_o[12 + rb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(tail_a), as_bf8(tail_b[rb]), acc_o[12 + rb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
           const u32x4 t = tv[ks % kPfS];
@@ -313,15 +347,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
           else mfma_s(acc_s, t, qreg[ks]);
           if ((ks & 3) == 2)
             copy16_to_lds(nbase, ld_off(ks >> 2), __builtin_amdgcn_readfirstlane(ndst + nstride * (ks >> 2)));
+          if (ks == 27) av[0] = rd(0);
+          if (ks == 31) av[1] = rd(1);
           if (ks == 32) {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) pb[0][rb] = lds_read16(pp + rb * 2048);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        settle_s(acc_s);
       }
       if (!valid || tok0 + kSubTok - 1 > L - sq) {   // past some row's last visible token, or no stage
+        settle_s(acc_s);   // the chain's result is read right away here
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int tok = tok0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -335,57 +371,66 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
       // step with the latent product of stage it - 1:
       //   O^T += C^T . P^T over this wave's 128 features (4 blocks of 32) x all 128 rows
       //   (4 row blocks) x 2 token halves, 32 MFMAs.  P comes from LDS, written there by
-      //   the wave that owns each row block.
-      uint32_t pk[8];
+      //   the wave that owns each row block.  The chain's result is first read after four
+      //   of these MFMAs, i.e. over a hundred cycles after the chain's last MFMA issued,
+      //   well past the wait an 8-pass MFMA's result needs.
       {
-        av[0] = rd(0);
-        av[1] = rd(1);
-        float z[16];
+        uint32_t pk[8];
+        float p[16];
         float mx = 0.0f, msafe = 0.0f;
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
+        for (int j = 0; j < 28; ++j) {
           const int hs = j >> 4, fb = (j >> 2) & 3, rb = j & 3, ai = 4 * hs + fb;
           acc_o[4 * fb + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(av[ai]), as_bf8(pb[hs][rb]),
                                                                        acc_o[4 * fb + rb], 0, 0, 0);
           if (rb == 0 && ai + 2 < 8) av[ai + 2] = rd(ai + 2);
-          if (j == 8) {
+          if (j == 10) {
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) pb[1][r2] = lds_read16(pp + r2 * 2048 + 1024);
           }
-          if (j < 4) {
-#pragma unroll
-            for (int r = 4 * j; r < 4 * j + 4; ++r) z[r] = acc_s[r];
-          } else if (j == 4) {
-            mx = __builtin_fmaxf(__builtin_fmaxf(z[0], __builtin_fmaxf(z[1], z[2])),
-                                 __builtin_fmaxf(__builtin_fmaxf(z[3], __builtin_fmaxf(z[4], z[5])), __builtin_fmaxf(z[6], z[7])));
-          } else if (j == 5) {
-            mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11])),
-                                 fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]))));
+          if (j == 5) {
+            mx = vmax3(vmax3(acc_s[0], acc_s[1], acc_s[2]), vmax3(acc_s[3], acc_s[4], acc_s[5]),
+                       vmax3(acc_s[6], acc_s[7], acc_s[8]));
           } else if (j == 6) {
+            mx = vmax3(mx, vmax3(acc_s[9], acc_s[10], acc_s[11]), vmax3(acc_s[12], acc_s[13], vmax2(acc_s[14], acc_s[15])));
+          } else if (j == 7) {
             // the other lane half holds the same row's other 16 tokens
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * zscale;   // zscale > 0
-            m_run = fmaxf(m_run, mx);
+            mx = vmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * zscale;   // zscale > 0
+          } else if (j == 9) {
+            m_run = vmax2(m_run, mx);
             m_ref = m_ref == kNegInf ? mx : m_ref;   // a row's reference: its first finite stage maximum
+          } else if (j == 11) {
             bad = bad || (mx > m_ref + kLazyTau);
             msafe = m_ref == kNegInf ? 0.0f : m_ref;
-          } else if (j < 29 && (j - 7) % 3 == 0) {
-            const int r = 2 * ((j - 7) / 3);
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[r], zscale, -msafe));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[r + 1], zscale, -msafe));
-            pk[r >> 1] = pack_bf2(p0, p1);
-            l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r >> 1]), kOnes2, l_sum, false);
-          } else if (j == 29) {
-            // this stage's weights, for every wave's latent product in the next iteration
-            *(MLA_LDS u32x4*)(pbuf + (it & 1) * kPBytes + wave * 2048 + lane * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-            *(MLA_LDS u32x4*)(pbuf + (it & 1) * kPBytes + wave * 2048 + 1024 + lane * 16) =
-                u32x4{pk[4], pk[5], pk[6], pk[7]};
+          } else if (j >= 12) {
+            // one weight per MFMA; each pair packed to bf16, and summed as rounded
+            const int r = j - 12;
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[r], zscale, -msafe));
+            if (r & 1) {
+              pk[r >> 1] = pack_bf2(p[r - 1], p[r]);
+              l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r >> 1]), kOnes2, l_sum, false);
+            }
+            if (j == 27) {
+              // this stage's weights, for every wave's latent product in the next iteration
+              *(MLA_LDS u32x4*)(pbuf + (it & 1) * kPBytes + wave * 2048 + lane * 16) =
+                  u32x4{pk[0], pk[1], pk[2], pk[3]};
+              *(MLA_LDS u32x4*)(pbuf + (it & 1) * kPBytes + wave * 2048 + 1024 + lane * 16) =
+                  u32x4{pk[4], pk[5], pk[6], pk[7]};
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        tail_a = av[7];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) tail_b[rb] = pb[1][rb];
       }
     }
+    // the last product's last four MFMAs
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      acc_o[12 + rb] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(tail_a), as_bf8(tail_b[rb]), acc_o[12 + rb], 0, 0, 0);
     const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0ull;
     // The last two iterations' copies (idle ones, into ring slots (nsub + 1) & 3 and
     // (nsub + 2) & 3) may still be in flight; they are asm, so the compiler does not wait
