@@ -457,18 +457,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     // (rounded to bf16 on the way out, through LDS: the ring is free once every wave has
     // left the loop, which the flag barriers above guarantee)
     uint16_t* prow = part_o + (size_t)piece * kRowsWG * kLat;
+    // two passes of 64 rows (two 32-row blocks staged side by side)
+    static_assert(2 * kEpiRows * kEpiStride <= kStages * kStageBytes, "two epilogue blocks fit the ring");
 #pragma unroll
-    for (int pass = 0; pass < kRowsWG / kEpiRows; ++pass) {
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        const f32x16& A = acc_o[4 * fb + pass];
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          stage_row_f4(lds, n, 128 * wave + 32 * fb + 8 * rr + 4 * hh,
-                       f32x4{A[4 * rr], A[4 * rr + 1], A[4 * rr + 2], A[4 * rr + 3]});
-      }
+        for (int fb = 0; fb < 4; ++fb) {
+          const f32x16& A = acc_o[4 * fb + 2 * pass + half];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            stage_row_f4(lds + half * kEpiRows * kEpiStride, n, 128 * wave + 32 * fb + 8 * rr + 4 * hh,
+                         f32x4{A[4 * rr], A[4 * rr + 1], A[4 * rr + 2], A[4 * rr + 3]});
+        }
       __syncthreads();
-      store_pass_bf16(lds, prow + (size_t)kEpiRows * pass * kLat, tid);
+      store_pass_bf16(lds, prow + (size_t)kEpiRows * 2 * pass * kLat, tid);
+      store_pass_bf16(lds + kEpiRows * kEpiStride, prow + (size_t)kEpiRows * (2 * pass + 1) * kLat, tid);
       __syncthreads();   // LDS free for the next pass (or the next range)
     }
     if (hh == 0) part_ml[(size_t)piece * kRowsWG + row] = make_float2(m_ref, l_tot);

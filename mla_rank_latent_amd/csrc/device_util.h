@@ -103,6 +103,11 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
   int quota = (total + num_wg - 1) / num_wg;
   quota = (quota + align - 1) / align * align;
   if (quota < align) quota = align;
+  // A range's partial state (128 rows x 512 bf16 latent sums) is 128 KB, which 114 cached
+  // tokens (1152 B each) would cost to read: ranges of the bf16 kernels take at least two
+  // 64-token blocks, so that small batches do not write (and merge) more partial-state bytes
+  // than the cache bytes they read.
+  if (align == kBlk && quota < kMinRangeTokens) quota = kMinRangeTokens;
   __syncthreads();
   // pass 2: pieces per sequence = number of ranges its segment meets
   if (t == 0) s_carry = 0;

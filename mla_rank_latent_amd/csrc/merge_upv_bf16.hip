@@ -97,7 +97,7 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float den = 0.0f, Mx = -__builtin_inff();
-    int p0 = 0, p1 = 0, r = 0;
+    int r = 0;
     const float2* part_ml = (const float2*)(ws + Lw.off_lse);
     const uint16_t* part_o = (const uint16_t*)(ws + Lw.off_o);   // bf16
     if (row_ok) {
@@ -106,83 +106,112 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
       const int g = h / hg;
       r = (h - g * hg) * sq + s;
       const int32_t* piece_base = (const int32_t*)(ws + Lw.off_piece);
-      p0 = g * P + piece_base[b];
-      p1 = g * P + piece_base[b + 1];
+      const int p0 = g * P + piece_base[b];
+      const int p1 = g * P + piece_base[b + 1];
       // online merge: the running maximum rises as pieces arrive and the sums so far are
-      // rescaled, so each pair's loads (states and weights together) need one round trip
-      for (int p = p0 + pl; p < p1; p += 2 * pl_n) {
-        // the second piece of the pair; past the end it re-reads piece p with weight 0
-        const int q = p + pl_n < p1 ? p + pl_n : p;
-        const float2 ml0 = part_ml[(size_t)p * Lw.rows + r];
-        const float2 ml1 = part_ml[(size_t)q * Lw.rows + r];
-        const u32x2* o0 = (const u32x2*)(part_o + ((size_t)p * Lw.rows + r) * kLat) + c16;
-        const u32x2* o1 = (const u32x2*)(part_o + ((size_t)q * Lw.rows + r) * kLat) + c16;
-        u32x2 b0[8], b1[8];
+      // rescaled; up to four pieces' loads (states and weights together) share one round trip
+      for (int p = p0 + pl; p < p1; p += 4 * pl_n) {
+        int q[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b0[j] = o0[16 * j];
+        for (int k = 0; k < 4; ++k) q[k] = p + k * pl_n < p1 ? p + k * pl_n : p;   // past the end: weight 0
+        float2 ml[4];
+        u32x2 bv[4][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b1[j] = o1[16 * j];
+        for (int k = 0; k < 4; ++k) ml[k] = part_ml[(size_t)q[k] * Lw.rows + r];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x2* o = (const u32x2*)(part_o + ((size_t)q[k] * Lw.rows + r) * kLat) + c16;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bv[k][j] = o[16 * j];
+        }
         // an empty piece has l = 0 (m = -inf, O = 0): weight 0
-        const float m0 = ml0.y > 0.0f ? ml0.x : -__builtin_inff();
-        const float m1 = (q != p && ml1.y > 0.0f) ? ml1.x : -__builtin_inff();
-        const float mn = fmaxf(Mx, fmaxf(m0, m1));
+        float mk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mk[k] = ((k == 0 || q[k] != p) && ml[k].y > 0.0f) ? ml[k].x : -__builtin_inff();
+        const float mn = fmaxf(fmaxf(Mx, fmaxf(mk[0], mk[1])), fmaxf(mk[2], mk[3]));
         if (mn == -__builtin_inff()) continue;   // nothing seen yet
         const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - mn);
-        const float w0 = m0 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m0 - mn);
-        const float w1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mn);
+        float w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = mk[k] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mk[k] - mn);
         auto widen = [](u32x2 v) {
           return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
                        __uint_as_float(v[1] & 0xffff0000u)};
         };
-        den = den * sc + w0 * ml0.y + w1 * ml1.y;
+        den = den * sc + w[0] * ml[0].y + w[1] * ml[1].y + w[2] * ml[2].y + w[3] * ml[3].y;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = acc[j] * sc + w0 * widen(b0[j]) + w1 * widen(b1[j]);
+        for (int j = 0; j < 8; ++j)
+          acc[j] = acc[j] * sc + w[0] * widen(bv[0][j]) + w[1] * widen(bv[1][j]) + w[2] * widen(bv[2][j]) +
+                   w[3] * widen(bv[3][j]);
         Mx = mn;
       }
     }
-    if (pl_n > 1) {   // bring the row's slots to the row's maximum
-      if (c16 == 0) s_mx[slot] = Mx;
-      __syncthreads();
-      float Mg = Mx;
-      for (int q = 0; q < pl_n; ++q) Mg = fmaxf(Mg, s_mx[q * rp + i]);
-      const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - Mg);
-      den *= sc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= sc;
-      Mx = Mg;
-    }
-    if (pl_n > 1) {   // sum the row's slots in slot order
-      MLA_LDS f32x4* comb = (MLA_LDS f32x4*)s_comb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) comb[(slot * 16 + c16) * 8 + j] = acc[j];
-      if (c16 == 0) s_den[slot] = den;
-      __syncthreads();
-      if (pl == 0) {
-        for (int q = 1; q < pl_n; ++q) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += comb[((q * rp + i) * 16 + c16) * 8 + j];
-          den += s_den[q * rp + i];
-        }
-      }
-    }
-    if (row_ok && pl == 0) {
-      if (c16 == 0 && lse != nullptr)
-        lse[(size_t)m * n_heads + h] =
-            den > 0.0f ? (Mx + __builtin_amdgcn_logf(den)) * 0.69314718055994531f : -__builtin_inff();
-      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-      // columns 64 j + 4 c16 .. +3 are half (c16 & 1) of logical chunk 8 j + c16 / 2,
-      // stored at chunk 8 j + ((c16 / 2) ^ (i % 8))
+    // the merged row, normalised, as a bf16 high part and remainder: columns 64 j + 4 c16 .. +3
+    // are half (c16 & 1) of logical chunk 8 j + c16 / 2, stored at chunk 8 j + ((c16 / 2) ^ (i % 8))
+    auto put_row = [&](int ii, int cc, const f32x4* a, float inv) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         u32x2 vh, vl;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float x0 = acc[j][2 * e] * inv, x1 = acc[j][2 * e + 1] * inv;
+          const float x0 = a[j][2 * e] * inv, x1 = a[j][2 * e + 1] * inv;
           const uint32_t hp = pack_bf2(x0, x1);
           vh[e] = hp;
           vl[e] = pack_bf2(x0 - bf2f((uint16_t)(hp & 0xffffu)), x1 - bf2f((uint16_t)(hp >> 16)));
         }
-        const int off = i * (kLat * 2) + (8 * j + ((c16 >> 1) ^ (i & 7))) * 16 + 8 * (c16 & 1);
+        const int off = ii * (kLat * 2) + (8 * j + ((cc >> 1) ^ (ii & 7))) * 16 + 8 * (cc & 1);
+        *(MLA_LDS u32x2*)(s_hi + off) = vh;
+        *(MLA_LDS u32x2*)(s_lo + off) = vl;
+      }
+    };
+    auto put_lse = [&](int mm, float mx, float dn) {
+      if (lse != nullptr)
+        lse[(size_t)mm * n_heads + h] = dn > 0.0f ? (mx + __builtin_amdgcn_logf(dn)) * 0.69314718055994531f
+                                                  : -__builtin_inff();
+    };
+    if (pl_n == 1) {
+      if (row_ok) {
+        if (c16 == 0) put_lse(m, Mx, den);
+        put_row(i, c16, acc, den > 0.0f ? 1.0f / den : 0.0f);
+      }
+    } else {
+      // A row's slots: brought to the row's maximum, their sums combined through LDS in slot
+      // order; every thread then finishes some (row, column-quad) pairs, so the combine's
+      // chain is pl_n reads long for 128 threads per row instead of 31 for 16.
+      if (c16 == 0) s_mx[slot] = Mx;
+      __syncthreads();
+      float Mg = Mx;
+      for (int q = 0; q < pl_n; ++q) Mg = fmaxf(Mg, s_mx[q * rp + i]);
+      const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - Mg);
+      MLA_LDS f32x4* comb = (MLA_LDS f32x4*)s_comb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) comb[(slot * 16 + c16) * 8 + j] = acc[j] * sc;
+      if (c16 == 0) s_den[slot] = den * sc;
+      __syncthreads();
+      for (int task = tid; task < rp * 128; task += 512) {
+        const int ii = task >> 7, quad = task & 127, jj = quad >> 4, cc = quad & 15;
+        if (ii >= rv) continue;
+        f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float dn = 0.0f;
+        for (int q = 0; q < pl_n; ++q) {
+          sum += comb[((q * rp + ii) * 16 + cc) * 8 + jj];
+          dn += s_den[q * rp + ii];
+        }
+        if (quad == 0) {
+          float mg = -__builtin_inff();
+          for (int q = 0; q < pl_n; ++q) mg = fmaxf(mg, s_mx[q * rp + ii]);
+          put_lse(mb * kMergeRows + ii, mg, dn);
+        }
+        const float inv = dn > 0.0f ? 1.0f / dn : 0.0f;
+        u32x2 vh, vl;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = sum[2 * e] * inv, x1 = sum[2 * e + 1] * inv;
+          const uint32_t hp = pack_bf2(x0, x1);
+          vh[e] = hp;
+          vl[e] = pack_bf2(x0 - bf2f((uint16_t)(hp & 0xffffu)), x1 - bf2f((uint16_t)(hp >> 16)));
+        }
+        const int off = ii * (kLat * 2) + (8 * jj + ((cc >> 1) ^ (ii & 7))) * 16 + 8 * (cc & 1);
         *(MLA_LDS u32x2*)(s_hi + off) = vh;
         *(MLA_LDS u32x2*)(s_lo + off) = vl;
       }

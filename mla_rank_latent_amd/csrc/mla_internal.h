@@ -24,6 +24,7 @@ constexpr int kStages = 4;           // LDS ring depth
 constexpr int kStageBytes = kSubTok * kRow * 2;        // 36864
 constexpr int kChunksPerRow = kRow * 2 / 16;           // 72 chunks of 16 B
 constexpr int kMaxSqBf16 = 8;
+constexpr int kMinRangeTokens = 2 * kBlk;   // smallest token range of the bf16 split plan
 // FP8 latent cache page (MLA_DTYPE_BF16_FP8): 64 rows of E4M3 codes, then 64 bf16
 // k^R rows, then 64 fp32 scales
 constexpr int kFp8RopeOff = kBlk * kLat;                       // 32768
