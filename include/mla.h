@@ -336,9 +336,13 @@ int mla_out_project(const mla_dims* dims, const void* o, const void* w_o, void* 
                     void* stream);
 
 /*
- * Workspace bytes mla_prefill needs: the expanded per-head keys and values of
- * every token slot the block table can address,
+ * Workspace bytes for the expanded per-head keys and values of every token slot
+ * the block table can address, for `batch` sequences:
  *   2 * batch * n_heads * (max_blocks * block_size) * d_nope * 2 bytes.
+ * mla_prefill_expand and mla_prefill_attend need it for the whole batch;
+ * mla_prefill runs with any workspace of at least one sequence's worth
+ * (mla_prefill_workspace_bytes(dims, 1, max_blocks)), taking the sequences in
+ * groups that fit, so its memory need not grow with the batch.
  * bf16 only; returns 0 for invalid arguments or f32 dims.
  */
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_blocks);
@@ -361,8 +365,12 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t 
  * w_uk, w_uv, cache, block_table, seq_lens, lse, status: as for mla_decode
  * softmax_scale  positive and finite (MLA_ERR_BAD_DIMS otherwise)
  * t          query tokens per sequence, 1 .. max_blocks * block_size
- * workspace  device scratch of at least mla_prefill_workspace_bytes(dims,
- *            batch, max_blocks) bytes, 256-byte aligned; clobbered
+ * workspace  device scratch, 256-byte aligned, clobbered: at least
+ *            mla_prefill_workspace_bytes(dims, 1, max_blocks) bytes (one
+ *            sequence); with less than the whole batch's
+ *            mla_prefill_workspace_bytes(dims, batch, max_blocks) the sequences
+ *            are expanded and attended in groups that fit, one after another on
+ *            the stream (same results)
  * out        [batch, t, n_heads, d_nope]   bf16
  * Limits: MLA_DTYPE_BF16 only (f32 and the FP8 cache: MLA_ERR_UNSUPPORTED);
  * max_blocks * block_size <= 2^23.
@@ -378,6 +386,8 @@ int mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope,
  * The two phases of mla_prefill, for callers that schedule or time them
  * separately.  Same arguments, checks and conventions; calling both in order
  * on one stream with the same arguments and workspace is exactly mla_prefill.
+ * The phases need the whole batch's workspace (MLA_ERR_WORKSPACE_TOO_SMALL
+ * otherwise), since expand writes every sequence before attend reads them.
  *  - expand: k^C_{j,i} = W^UK_i c_j and v_{j,i} = W^UV_i c_j for every context
  *    token j and head i ("DeepSeek-V2 ... MLA" page §2.1), into the workspace.
  *  - attend: causal attention of the t queries over [k^C_{j,i} ‖ k^R_j] and

@@ -497,19 +497,37 @@ int prefill_phases(int phases, const mla_dims* dims, const void* q_nope, const v
       !aligned16(block_table) || !aligned16(seq_lens) || !aligned16(out) || ((uintptr_t)workspace & (kAlign - 1)) ||
       (lse && ((uintptr_t)lse & 3u)) || (status && ((uintptr_t)status & 3u)))
     return MLA_ERR_BAD_ALIGN;
-  const size_t need = prefill_ws_bytes(batch, dims->n_heads, max_blocks);
-  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  // The expanded keys and values of one sequence take per_seq bytes.  The phase calls need
+  // room for every sequence (expand writes them all before attend reads them); the whole
+  // call processes the sequences in groups that fit the workspace given, each group
+  // expanded and then attended, so its workspace need not grow with the batch.
+  const size_t per_seq = prefill_ws_bytes(1, dims->n_heads, max_blocks);
+  const bool both = (phases & kPrefillExpand) && (phases & kPrefillAttend);
+  int group = batch;
+  if (workspace_bytes < prefill_ws_bytes(batch, dims->n_heads, max_blocks)) {
+    if (!both || workspace_bytes < per_seq) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    group = (int)(workspace_bytes / per_seq);
+  }
   hipStream_t st = (hipStream_t)stream;
-  uint16_t* kc = (uint16_t*)workspace;
-  uint16_t* vt = kc + need / 4;   // the second half: V^T
+  const int H = dims->n_heads;
   hipError_t e = hipSuccess;
-  if (phases & kPrefillExpand)
-    e = launch_expand_kv_bf16((const uint16_t*)cache, num_blocks, block_table, max_blocks, seq_lens, batch,
-                              dims->n_heads, (const uint16_t*)w_uk, (const uint16_t*)w_uv, kc, vt, status, st);
-  if (e == hipSuccess && (phases & kPrefillAttend))
-    e = launch_prefill_attn_bf16((const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)cache,
-                                 num_blocks, block_table, max_blocks, seq_lens, batch, t, dims->n_heads,
-                                 softmax_scale, kc, vt, (uint16_t*)out, lse, status, st);
+  for (int b0 = 0; b0 < batch && e == hipSuccess; b0 += group) {
+    const int nb = batch - b0 < group ? batch - b0 : group;
+    uint16_t* kc = (uint16_t*)workspace;
+    uint16_t* vt = kc + prefill_ws_bytes(nb, H, max_blocks) / 4;   // the second half: V^T
+    const int32_t* bt = block_table + (size_t)b0 * max_blocks;
+    const int32_t* lens = seq_lens + b0;
+    if (phases & kPrefillExpand)
+      e = launch_expand_kv_bf16((const uint16_t*)cache, num_blocks, bt, max_blocks, lens, nb, H,
+                                (const uint16_t*)w_uk, (const uint16_t*)w_uv, kc, vt, status, st);
+    if (e == hipSuccess && (phases & kPrefillAttend)) {
+      const size_t rows = (size_t)b0 * t * H;   // query rows before this group
+      e = launch_prefill_attn_bf16((const uint16_t*)q_nope + rows * dims->d_nope,
+                                   (const uint16_t*)q_rope + rows * dims->d_rope, (const uint16_t*)cache, num_blocks,
+                                   bt, max_blocks, lens, nb, t, H, softmax_scale, kc, vt,
+                                   (uint16_t*)out + rows * dims->d_nope, lse ? lse + rows : nullptr, status, st);
+    }
+  }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -134,7 +134,9 @@ def test_prefill_workspace_and_argument_errors():
         assert _prefill(v2, fn, batch=0) == -2
         assert _prefill(v2, fn, out=FAKE + 4) == -4
         assert _prefill(v2, fn, ws=FAKE + 128) == -4
-        assert _prefill(v2, fn, ws_bytes=need - 1) == -5
+        # the phases need the whole batch's workspace; the whole call one sequence's worth
+        per_seq = mla.mla_prefill_workspace_bytes(v2, 1, 4)
+        assert _prefill(v2, fn, ws_bytes=(per_seq - 1) if fn == "mla_prefill" else need - 1) == -5
         assert _prefill(v2, fn, max_blocks=(1 << 17) + 1, num_blocks=1 << 18) == -6
         assert _prefill(mla.dims(8, 16, 8, 32, 64, dtype="f32"), fn) == -8
         assert _prefill(mla.dims(128, 128, 64, 512, 5120, block_size=32), fn) == -8

@@ -124,3 +124,52 @@ def test_prefill_full_size_every_tile_every_head():
     H.log(f"  lse max-abs {d:.3e}")
     assert d <= 2e-2
     assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("group", [1, 3])
+def test_prefill_in_groups_of_sequences(group):
+    """mla_prefill with a workspace for `group` sequences (fewer than the batch) expands and
+    attends the sequences group by group: the output equals the one-workspace run bit for bit
+    and matches the oracle."""
+    import torch
+    from mla_rank_latent_amd import mla
+    x = synth.make_inputs(_spec("prefill_groups", [700, 300, 1000, 129, 512], 128, n_heads=16, seed=81))
+    full = _run(x)
+    out_full, lse_full = full.out.clone(), full.lse.clone()
+    c = H.PrefillCase(x)
+    per_seq = mla.mla_prefill_workspace_bytes(c.d, 1, int(x["block_table"].shape[1]))
+    c.ws = torch.empty(group * per_seq, dtype=torch.uint8, device="cuda")
+    H.log(f"prefill_groups: workspace for {group} of {x['spec'].batch} sequences")
+    c.run()
+    torch.cuda.synchronize()
+    assert int(c.status.item()) == 0
+    assert torch.equal(c.out.view(torch.int16), out_full.view(torch.int16))
+    assert torch.equal(c.lse, lse_full)
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", f"prefill in groups of {group}")
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
+@pytest.mark.timeout(900)
+def test_prefill_batch8_ctx8192_in_one_sequence_workspace():
+    """Eight 8192-token sequences, the last 1024 tokens of each a query (a chunked-prefill
+    step over a batch), with a workspace that holds one sequence's expanded keys and values
+    (537 MB at 128 heads, an eighth of the batch's): every sequence is checked against the
+    oracle on four queries spread over its group, every head."""
+    import torch
+    from mla_rank_latent_amd import mla
+    x = synth.make_inputs(_spec("prefill_b8_ctx8192", [8192] * 8, 1024, seed=83))
+    c = H.PrefillCase(x)
+    per_seq = mla.mla_prefill_workspace_bytes(c.d, 1, int(x["block_table"].shape[1]))
+    c.ws = torch.empty(per_seq, dtype=torch.uint8, device="cuda")
+    H.log(f"prefill_b8_ctx8192: workspace {per_seq} bytes (one of 8 sequences)")
+    c.run()
+    torch.cuda.synchronize()
+    assert int(c.status.item()) == 0
+    out, lse = H.host(c.out), H.host(c.lse)
+    assert np.all(np.isfinite(out))
+    for b in range(8):
+        queries = [0, 300 + 50 * b, 700, 1023]
+        want, want_lse = H.oracle_single_queries(x, b, queries)
+        H.assert_close(out[b, queries], want, "bf16", f"prefill_b8 sequence {b}")
+        assert np.max(np.abs(lse[b, queries] - want_lse)) <= 2e-2
