@@ -302,7 +302,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
         const int ntl = tlast_of(it + 2);
         if (ntl < kSubTok - 1) set_ld_off(ntl);   // the range's last stage: later copies are idle
       }
-      if (it + 3 < nsub) blk_next = lookup_block(b, a + (it + 3) * kSubTok);
       const bool valid = it < nsub;
       const MLA_LDS uint8_t* st = lds + (it & 3) * kStageBytes;
       // the latent product's stage (stage 0 for the empty product of iteration 0:
@@ -425,6 +424,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) tail_b[rb] = pb[1][rb];
       }
+      // The block id of stage it + 3 (its copies go out in the next iteration).  A scalar
+      // load is counted with the LDS reads and returns out of order, so any LDS wait after
+      // it must wait for it too: issued here, its latency hides under the barrier's wait
+      // instead of the next score chain's first operand wait.
+      if (it + 3 < nsub) blk_next = lookup_block(b, a + (it + 3) * kSubTok);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the last product's last four MFMAs
 #pragma unroll
