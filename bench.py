@@ -575,14 +575,22 @@ def main() -> int:
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     out = torch.empty(spec.batch, spec.sq, spec.n_heads, spec.d_nope, dtype=tdt, device="cuda")
     lse = torch.empty(spec.batch, spec.sq, spec.n_heads, dtype=torch.float32, device="cuda")
-    ws = torch.empty(mla.mla_decode_workspace_bytes(d, spec.batch, spec.sq, args.num_splits), dtype=torch.uint8,
-                     device="cuda")
     stream = torch.cuda.current_stream()
     has_append = spec.append
+    # a bf16 step that appends its own tokens runs as mla_decode_step (the append's partial
+    # products, the absorbed queries and the split plan in one launch); the FP8 cache appends
+    # with mla_cache_append, then decodes
+    fused = has_append and not fp8
+    if fused:
+        ws = torch.empty(mla.mla_decode_step_workspace_bytes(d, spec.batch, spec.sq, args.num_splits),
+                         dtype=torch.uint8, device="cuda")
+    else:
+        ws = torch.empty(mla.mla_decode_workspace_bytes(d, spec.batch, spec.sq, args.num_splits), dtype=torch.uint8,
+                         device="cuda")
     append_ws = None
     if has_append:
         n_ws = mla.mla_cache_append_workspace_bytes(d, spec.batch, spec.sq)
-        append_ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws else None
+        append_ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws and not fused else None
         pos = dev(x["positions"])
 
     # Every copy holds its own cache, queries, weights and hidden states (each step reads one
@@ -606,12 +614,20 @@ def main() -> int:
         else:
             t = {key: v.clone() for key, v in base.items()}
         launches = []
-        if has_append:
-            launches.append(mla.prepared_cache_append(d, t["h"], t["w_dkv"], t["w_kr"], pos, bt, t["pool"],
-                                                      workspace=append_ws, stream=stream))
-        dec_args = (d, t["qn"], t["qr"], t["w_uk"], t["w_uv"], t["pool"], bt, lens, x["scale"], ws, out)
-        for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
-            launches.append(mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits, stream=stream))
+        if fused:
+            for ph in (mla.MLA_PHASE_PREPARE, mla.MLA_PHASE_ATTEND, mla.MLA_PHASE_FINISH):
+                launches.append(mla.prepared_decode_step(d, t["h"], t["w_dkv"], t["w_kr"], pos, t["qn"], t["qr"],
+                                                         t["w_uk"], t["w_uv"], t["pool"], bt, lens, x["scale"], ws,
+                                                         out, lse=lse, num_splits=args.num_splits, phases=ph,
+                                                         stream=stream))
+        else:
+            if has_append:
+                launches.append(mla.prepared_cache_append(d, t["h"], t["w_dkv"], t["w_kr"], pos, bt, t["pool"],
+                                                          workspace=append_ws, stream=stream))
+            dec_args = (d, t["qn"], t["qr"], t["w_uk"], t["w_uv"], t["pool"], bt, lens, x["scale"], ws, out)
+            for name in ("mla_decode_prepare", "mla_decode_attend", "mla_decode_finish"):
+                launches.append(mla.prepared_decode(name, *dec_args, lse=lse, num_splits=args.num_splits,
+                                                    stream=stream))
         sets.append(launches)
     torch.cuda.synchronize()
     counter = [0]
@@ -619,7 +635,7 @@ def main() -> int:
     def step(ev_a=None, ev_b=None):
         launches = sets[counter[0] % copies]
         counter[0] += 1
-        for launch in launches[:-2]:      # append (if any), then prepare
+        for launch in launches[:-2]:      # append (if not fused into the step), then prepare
             launch()
         if ev_a is not None:
             ev_a.record(stream)

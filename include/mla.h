@@ -277,6 +277,60 @@ int mla_decode_finish(const mla_dims* dims, const void* q_nope, const void* q_ro
                       int32_t* status, void* stream);
 
 /*
+ * A decode step that appends its own tokens: exactly mla_cache_append of the sq new
+ * tokens of every sequence (t = sq, with a workspace) followed by mla_decode of those
+ * tokens as the query group, bit for bit the same results, in fewer launches.
+ * ("DeepSeek-V2: Multi-Head Latent Attention (MLA) 原理与工程实现" §2.1 and §3.2 for
+ * the cached row of a new token, §2.2 for the absorbed decode.)  The append's partial
+ * products, the absorbed queries and the split plan depend on nothing from one another
+ * and run in one launch.  MLA_DTYPE_BF16 only (others: MLA_ERR_UNSUPPORTED).
+ *
+ * Each field means what the argument of the same name means for mla_cache_append
+ * (h, w_dkv, w_kr, positions; t = sq) or mla_decode (the rest); seq_lens include the
+ * new tokens.  workspace: at least mla_decode_step_workspace_bytes(dims, batch, sq,
+ * num_splits) bytes, 256-byte aligned, clobbered.  Every argument is checked on the host
+ * before anything is launched, as by those two calls.
+ * phases: MLA_PHASE_ALL, or any of
+ *  - MLA_PHASE_PREPARE: the new rows written to the cache, the absorbed queries and the
+ *    split plan (into the workspace);
+ *  - MLA_PHASE_ATTEND / MLA_PHASE_FINISH: mla_decode_attend / mla_decode_finish.
+ * Calling the phases in order on one stream with the same arguments equals MLA_PHASE_ALL.
+ */
+typedef struct mla_step_args {
+  const void* h;               /* [batch, sq, d_model]                          */
+  const void* w_dkv;           /* [d_latent, d_model]                           */
+  const void* w_kr;            /* [d_rope, d_model]                             */
+  const int32_t* positions;    /* [batch, sq] int32 (device)                    */
+  const void* q_nope;          /* [batch, sq, n_heads, d_nope]                  */
+  const void* q_rope;          /* [batch, sq, n_heads, d_rope], rotated         */
+  const void* w_uk;            /* [n_heads * d_nope, d_latent]                  */
+  const void* w_uv;            /* [n_heads * d_nope, d_latent]                  */
+  void* cache;                 /* [num_blocks, block_size, d_latent + d_rope]   */
+  int32_t num_blocks;
+  const int32_t* block_table;  /* [batch, max_blocks] int32 (device)            */
+  int32_t max_blocks;
+  const int32_t* seq_lens;     /* [batch] int32 (device), new tokens included   */
+  int32_t batch;
+  int32_t sq;                  /* new tokens = query tokens per sequence        */
+  float softmax_scale;
+  int32_t num_splits;
+  void* workspace;
+  size_t workspace_bytes;
+  void* out;                   /* [batch, sq, n_heads, d_nope]                  */
+  float* lse;                  /* optional [batch, sq, n_heads]                 */
+  int32_t* status;             /* optional                                      */
+} mla_step_args;
+
+#define MLA_PHASE_PREPARE 1
+#define MLA_PHASE_ATTEND  2
+#define MLA_PHASE_FINISH  4
+#define MLA_PHASE_ALL     7
+
+/* Workspace bytes mla_decode_step needs (0 for invalid arguments or non-bf16 dims). */
+size_t mla_decode_step_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t sq, int32_t num_splits);
+int mla_decode_step(const mla_dims* dims, const mla_step_args* args, int32_t phases, void* stream);
+
+/*
  * mla_decode without a caller workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  Same arguments, checks, results and conventions as mla_decode with

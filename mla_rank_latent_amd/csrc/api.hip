@@ -184,11 +184,14 @@ size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t batch, int
   return split;
 }
 
-int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr, const int32_t* positions,
-                     const int32_t* block_table, int32_t max_blocks, void* cache, int32_t num_blocks, int32_t batch,
-                     int32_t t, void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
-  int rc = check_dims(dims);
-  if (rc != MLA_OK) return rc;
+}  // extern "C"
+
+namespace {
+// mla_cache_append's argument checks (dims checked already)
+int check_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr, const int32_t* positions,
+                 const int32_t* block_table, int32_t max_blocks, const void* cache, int32_t num_blocks,
+                 int32_t batch, int32_t t, const void* workspace, const int32_t* status) {
+  int rc;
   if (!h || !w_dkv || !w_kr || !positions || !block_table || !cache) return MLA_ERR_NULL_PTR;
   if (t < 1) return MLA_ERR_BAD_DIMS;
   if ((rc = check_pool(dims, num_blocks, max_blocks, batch)) != MLA_OK) return rc;
@@ -196,6 +199,20 @@ int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, con
   if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(positions) || !aligned16(block_table) ||
       !aligned16(cache) || (status && ((uintptr_t)status & 3u)) || (workspace && !aligned16(workspace)))
     return MLA_ERR_BAD_ALIGN;
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mla_cache_append(const mla_dims* dims, const void* h, const void* w_dkv, const void* w_kr, const int32_t* positions,
+                     const int32_t* block_table, int32_t max_blocks, void* cache, int32_t num_blocks, int32_t batch,
+                     int32_t t, void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if ((rc = check_append(dims, h, w_dkv, w_kr, positions, block_table, max_blocks, cache, num_blocks, batch, t,
+                         workspace, status)) != MLA_OK)
+    return rc;
   const bool gemm = append_uses_gemm(dims, (long long)batch * t);
   hipStream_t st = (hipStream_t)stream;
   if (is_fp8(dims)) {
@@ -445,6 +462,62 @@ int mla_decode(MLA_DECODE_PARAMS) {
 int mla_decode_prepare(MLA_DECODE_PARAMS) { return decode_impl(kPhasePrepare, false, MLA_DECODE_ARGS); }
 int mla_decode_attend(MLA_DECODE_PARAMS) { return decode_impl(kPhaseAttend, false, MLA_DECODE_ARGS); }
 int mla_decode_finish(MLA_DECODE_PARAMS) { return decode_impl(kPhaseFinish, false, MLA_DECODE_ARGS); }
+
+size_t mla_decode_step_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t sq, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || dims->dtype != MLA_DTYPE_BF16) return 0;
+  const size_t dec = mla_decode_workspace_bytes(dims, batch, sq, num_splits);
+  if (dec == 0 || (long long)batch * sq >= (1ll << 30)) return 0;
+  const long long tokens = (long long)batch * sq;
+  return up(dec) + (append_uses_gemm(dims, tokens) ? 0 : up(append_split_ws_bytes(dims->d_model, tokens)));
+}
+
+int mla_decode_step(const mla_dims* dims, const mla_step_args* args, int32_t phases, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MLA_OK) return rc;
+  if (args == nullptr) return MLA_ERR_NULL_PTR;
+  if (dims->dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (phases < 1 || phases > (kPhasePrepare | kPhaseAttend | kPhaseFinish)) return MLA_ERR_BAD_DIMS;
+  const mla_step_args& a = *args;
+  // the append's checks (t = sq tokens per sequence), then decode's, without launching anything
+  if ((rc = check_append(dims, a.h, a.w_dkv, a.w_kr, a.positions, a.block_table, a.max_blocks, a.cache,
+                         a.num_blocks, a.batch, a.sq, a.workspace, a.status)) != MLA_OK)
+    return rc;
+  if ((rc = decode_impl(0, false, dims, a.q_nope, a.q_rope, a.w_uk, a.w_uv, a.cache, a.num_blocks, a.block_table,
+                        a.max_blocks, a.seq_lens, a.batch, a.sq, a.softmax_scale, a.num_splits, a.workspace,
+                        a.workspace_bytes, a.out, a.lse, a.status, stream)) != MLA_OK)
+    return rc;
+  if (a.workspace_bytes < mla_decode_step_workspace_bytes(dims, a.batch, a.sq, a.num_splits))
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+  WsLayout L;
+  if (!ws_layout(dims, a.batch, a.sq, a.num_splits, &L)) return MLA_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)a.workspace;
+  hipError_t e = hipSuccess;
+  if (phases & kPhasePrepare) {
+    float qscale, zscale;
+    split_softmax_scale(a.softmax_scale, &qscale, &zscale);
+    const uint16_t *h = (const uint16_t*)a.h, *w_dkv = (const uint16_t*)a.w_dkv, *w_kr = (const uint16_t*)a.w_kr;
+    if (append_uses_gemm(dims, (long long)a.batch * a.sq)) {
+      // many tokens: mla_cache_append's GEMM path, then the absorbed queries and the plan
+      e = launch_append_gemm_bf16(h, w_dkv, w_kr, a.positions, a.block_table, a.max_blocks, (uint16_t*)a.cache,
+                                  a.num_blocks, a.batch * a.sq, a.sq, dims->d_model, dims->rope_base, a.status, st);
+      if (e == hipSuccess)
+        e = launch_absorb_bf16(L, (const uint16_t*)a.q_nope, (const uint16_t*)a.q_rope, (const uint16_t*)a.w_uk,
+                               a.seq_lens, a.max_blocks, a.batch, a.sq, dims->n_heads, qscale, ws, a.status, st);
+    } else {
+      e = launch_step_prepare_bf16(h, w_dkv, w_kr, a.positions, a.block_table, a.max_blocks, (uint16_t*)a.cache,
+                                   a.num_blocks, a.sq, dims->d_model, dims->rope_base, (float*)(ws + up(L.total)), L,
+                                   (const uint16_t*)a.q_nope, (const uint16_t*)a.q_rope, (const uint16_t*)a.w_uk,
+                                   a.seq_lens, a.batch, a.sq, dims->n_heads, qscale, ws, a.status, st);
+    }
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (phases & (kPhaseAttend | kPhaseFinish))
+    return decode_impl(phases & (kPhaseAttend | kPhaseFinish), false, dims, a.q_nope, a.q_rope, a.w_uk, a.w_uv,
+                       a.cache, a.num_blocks, a.block_table, a.max_blocks, a.seq_lens, a.batch, a.sq, a.softmax_scale,
+                       a.num_splits, a.workspace, a.workspace_bytes, a.out, a.lse, a.status, stream);
+  return MLA_OK;
+}
 
 int mla_decode_noalloc(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
                        const void* w_uv, const void* cache, int32_t num_blocks, const int32_t* block_table,

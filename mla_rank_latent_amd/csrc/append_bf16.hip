@@ -14,7 +14,7 @@
 // RoPE pairs (x_{2i}, x_{2i+1}) turn by angle p * base^(-2i/64), with the angle,
 // its sine and cosine and the rotation in fp64; each value is then rounded
 // once to bf16.
-#include "device_util.h"
+#include "prep_tiles.h"
 
 namespace mla {
 
@@ -130,75 +130,13 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_bf16_kernel(
 // timing), applies RoPE to the k^R pairs and writes the bf16 rows.
 // Workspace layout: [token][slice][576] fp32.
 // ---------------------------------------------------------------------------
-namespace {
-constexpr int kSliceSteps = 10;                    // k-steps (32 elements) per K slice, at most
-constexpr int kSliceChunks = 4 * kSliceSteps + 1;  // 16-byte chunks per padded LDS row
-constexpr int kTileRows = 64 + 32;                 // tokens + weight rows of one tile
-}  // namespace
-
 __global__ __launch_bounds__(256) void append_partial_bf16_kernel(const uint16_t* __restrict__ h,
                                                                   const uint16_t* __restrict__ w_dkv,
                                                                   const uint16_t* __restrict__ w_kr, int tokens,
                                                                   int d_model, int nslice, float* __restrict__ part) {
-  // whole 1 KB copies: the lanes of the last copy past the tile still write their 16 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t smem[(kTileRows * kSliceChunks + 63) / 64 * 1024];
-  MLA_LDS uint8_t* lds = (MLA_LDS uint8_t*)smem;
-  const int ct = blockIdx.x;   // 32-column tile of the 576-wide row
-  const int tg = blockIdx.y;   // 64-token group
-  const int sl = blockIdx.z;   // K slice
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int nks = d_model / 32;
-  const int k0 = (int)((long long)sl * nks / nslice), k1 = (int)((long long)(sl + 1) * nks / nslice);
-  const int nsteps = k1 - k0;                       // 1 .. kSliceSteps
-  const int rch = 4 * nsteps + 1;                   // chunks per padded LDS row (odd)
-
-  // copy: LDS chunk P = 64 q + lane holds row P / rch, chunk P % rch (the last chunk of a
-  // row is padding: it re-reads the row's first chunk)
-  const int nchunks = kTileRows * rch;
-  for (int q = wave; q * 64 < nchunks; q += 4) {
-    int P = q * 64 + lane;
-    if (P >= nchunks) P = nchunks - 1;              // the tail lanes repeat the last chunk
-    const int row = P / rch;
-    int ch = P - row * rch;
-    if (ch == rch - 1) ch = 0;
-    const uint16_t* src;
-    if (row < 64) {
-      const int tok = tg * 64 + row;
-      src = h + (size_t)(tok < tokens ? tok : 0) * d_model;
-    } else {
-      const int col = ct * 32 + (row - 64);
-      src = col < kLat ? w_dkv + (size_t)col * d_model : w_kr + (size_t)(col - kLat) * d_model;
-    }
-    src += 32 * k0 + 8 * ch;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + q * 1024));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
-  }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __syncthreads();
-
-  // wave w: tokens 16 w .. +15 (A rows) against the 32 columns (two 16-wide B blocks)
-  const bool tok_ok = tg * 64 + wave * 16 + (lane & 15) < tokens;
-  const MLA_LDS uint8_t* arow = lds + (wave * 16 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
-  const MLA_LDS uint8_t* brow0 = lds + (64 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
-  const MLA_LDS uint8_t* brow1 = brow0 + 16 * rch * 16;
-  f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int ks = 0; ks < nsteps; ++ks) {
-    u32x4 a = *(const MLA_LDS u32x4*)(arow + 64 * ks);
-    const u32x4 b0 = *(const MLA_LDS u32x4*)(brow0 + 64 * ks);
-    const u32x4 b1 = *(const MLA_LDS u32x4*)(brow1 + 64 * ks);
-    if (!tok_ok) a = u32x4{0u, 0u, 0u, 0u};
-    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b0), acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b1), acc[1], 0, 0, 0);
-  }
-  // D: lane holds column lane % 16 of its 16-column block, tokens 4 (lane / 16) + r of the wave's 16
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = tg * 64 + wave * 16 + 4 * (lane >> 4) + r;
-      if (t < tokens) part[((size_t)t * nslice + sl) * kRow + ct * 32 + nb * 16 + (lane & 15)] = acc[nb][r];
-    }
+  __shared__ __attribute__((aligned(16))) uint8_t smem[prep::kAppendPartialLds];
+  prep::append_partial_tile(h, w_dkv, w_kr, tokens, d_model, nslice, part, (MLA_LDS uint8_t*)smem, blockIdx.x,
+                            blockIdx.y, blockIdx.z);
 }
 
 __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __restrict__ part, int nslice,
@@ -391,7 +329,7 @@ hipError_t launch_append_gemm_bf16(const uint16_t* h, const uint16_t* w_dkv, con
 
 int append_split_slices(int d_model) {
   const int nks = d_model / 32;
-  return (nks + kSliceSteps - 1) / kSliceSteps;
+  return (nks + prep::kSliceSteps - 1) / prep::kSliceSteps;
 }
 
 size_t append_split_ws_bytes(int d_model, long long tokens) {
@@ -408,10 +346,17 @@ hipError_t launch_append_split_bf16(const uint16_t* h, const uint16_t* w_dkv, co
                      ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_append_finish_bf16(ws, nslice, positions, block_table, max_blocks, cache, num_blocks, tokens,
+                                   t_per_seq, rope_base, status, st);
+}
+
+hipError_t launch_append_finish_bf16(const float* part, int nslice, const int32_t* positions,
+                                     const int32_t* block_table, int max_blocks, uint16_t* cache, int num_blocks,
+                                     int tokens, int t_per_seq, float rope_base, int32_t* status, hipStream_t st) {
   const long long items = (long long)tokens * (kRow / 2);
   dim3 grid2((unsigned)((items + 255) / 256));
-  hipLaunchKernelGGL(append_finish_bf16_kernel, grid2, dim3(256), 0, st, (const float*)ws, nslice, positions,
-                     block_table, max_blocks, cache, num_blocks, tokens, t_per_seq, (double)rope_base, status);
+  hipLaunchKernelGGL(append_finish_bf16_kernel, grid2, dim3(256), 0, st, part, nslice, positions, block_table,
+                     max_blocks, cache, num_blocks, tokens, t_per_seq, (double)rope_base, status);
   return hipGetLastError();
 }
 

@@ -72,6 +72,18 @@ hipError_t launch_append_split_bf16(const uint16_t* h, const uint16_t* w_dkv, co
                                     const int32_t* positions, const int32_t* block_table, int max_blocks,
                                     uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
                                     float rope_base, float* ws, int32_t* status, hipStream_t st);
+// the split append's second kernel alone (the slices summed in order, RoPE, the rows written)
+hipError_t launch_append_finish_bf16(const float* part, int nslice, const int32_t* positions,
+                                     const int32_t* block_table, int max_blocks, uint16_t* cache, int num_blocks,
+                                     int tokens, int t_per_seq, float rope_base, int32_t* status, hipStream_t st);
+// a decode step's append partial products, absorbed queries and split plan in one launch,
+// then the append's second kernel
+hipError_t launch_step_prepare_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
+                                    const int32_t* positions, const int32_t* block_table, int max_blocks,
+                                    uint16_t* cache, int num_blocks, int t_per_seq, int d_model, float rope_base,
+                                    float* part, const WsLayout& L, const uint16_t* q_nope, const uint16_t* q_rope,
+                                    const uint16_t* w_uk, const int32_t* seq_lens, int batch, int sq, int n_heads,
+                                    float qscale, uint8_t* ws, int32_t* status, hipStream_t st);
 hipError_t launch_append_bf16(const uint16_t* h, const uint16_t* w_dkv, const uint16_t* w_kr,
                               const int32_t* positions, const int32_t* block_table, int max_blocks,
                               uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,

@@ -1,0 +1,218 @@
+// Tiles of a decode step's preparation, shared by the kernels that run them alone
+// (the split append's partial products, the absorbed queries) and by the kernel that
+// runs them side by side in one launch (a decode step that appends its own tokens).
+// What they compute is described at the kernels in append_bf16.hip and absorb_bf16.hip.
+#pragma once
+
+#include "device_util.h"
+
+namespace mla {
+namespace prep {
+
+__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---- split append: K slices of at most kSliceSteps k-steps (32 elements) of d_model
+constexpr int kSliceSteps = 10;
+constexpr int kSliceChunks = 4 * kSliceSteps + 1;  // 16-byte chunks per padded LDS row
+constexpr int kTileRows = 64 + 32;                 // tokens + weight rows of one tile
+constexpr int kAppendPartialLds = (kTileRows * kSliceChunks + 63) / 64 * 1024;
+
+// One [64 tokens x 32 columns] partial product over K slice sl of the split append:
+// ct = 32-column tile of the 576-wide row, tg = 64-token group; lds holds
+// kAppendPartialLds bytes (whole 1 KB copies: the lanes of the last copy past the tile
+// still write their 16 bytes).
+__device__ __forceinline__ void append_partial_tile(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
+                                                    const uint16_t* __restrict__ w_kr, int tokens, int d_model,
+                                                    int nslice, float* __restrict__ part, MLA_LDS uint8_t* lds, int ct,
+                                                    int tg, int sl) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nks = d_model / 32;
+  const int k0 = (int)((long long)sl * nks / nslice), k1 = (int)((long long)(sl + 1) * nks / nslice);
+  const int nsteps = k1 - k0;                       // 1 .. kSliceSteps
+  const int rch = 4 * nsteps + 1;                   // chunks per padded LDS row (odd)
+
+  // copy: LDS chunk P = 64 q + lane holds row P / rch, chunk P % rch (the last chunk of a
+  // row is padding: it re-reads the row's first chunk)
+  const int nchunks = kTileRows * rch;
+  for (int q = wave; q * 64 < nchunks; q += 4) {
+    int P = q * 64 + lane;
+    if (P >= nchunks) P = nchunks - 1;              // the tail lanes repeat the last chunk
+    const int row = P / rch;
+    int ch = P - row * rch;
+    if (ch == rch - 1) ch = 0;
+    const uint16_t* src;
+    if (row < 64) {
+      const int tok = tg * 64 + row;
+      src = h + (size_t)(tok < tokens ? tok : 0) * d_model;
+    } else {
+      const int col = ct * 32 + (row - 64);
+      src = col < kLat ? w_dkv + (size_t)col * d_model : w_kr + (size_t)(col - kLat) * d_model;
+    }
+    src += 32 * k0 + 8 * ch;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + q * 1024));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  // wave w: tokens 16 w .. +15 (A rows) against the 32 columns (two 16-wide B blocks)
+  const bool tok_ok = tg * 64 + wave * 16 + (lane & 15) < tokens;
+  const MLA_LDS uint8_t* arow = lds + (wave * 16 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
+  const MLA_LDS uint8_t* brow0 = lds + (64 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
+  const MLA_LDS uint8_t* brow1 = brow0 + 16 * rch * 16;
+  f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int ks = 0; ks < nsteps; ++ks) {
+    u32x4 a = *(const MLA_LDS u32x4*)(arow + 64 * ks);
+    const u32x4 b0 = *(const MLA_LDS u32x4*)(brow0 + 64 * ks);
+    const u32x4 b1 = *(const MLA_LDS u32x4*)(brow1 + 64 * ks);
+    if (!tok_ok) a = u32x4{0u, 0u, 0u, 0u};
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b0), acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b1), acc[1], 0, 0, 0);
+  }
+  // D: lane holds column lane % 16 of its 16-column block, tokens 4 (lane / 16) + r of the wave's 16
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tg * 64 + wave * 16 + 4 * (lane >> 4) + r;
+      if (t < tokens) part[((size_t)t * nslice + sl) * kRow + ct * 32 + nb * 16 + (lane & 15)] = acc[nb][r];
+    }
+}
+
+// ---- absorbed queries
+constexpr int kAbsorbLds = kNope * 256 + 2 * 64 * kNope * 2;
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// One (head, 128 latent columns) block of the absorbed queries; bid = 0 .. 4 n_heads - 1;
+// lds holds kAbsorbLds bytes, 1 KB aligned.
+__device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+                                            const uint16_t* __restrict__ w_uk, int batch, int sq, int n_heads,
+                                            float qscale, uint8_t* __restrict__ ws, const WsLayout& Lw,
+                                            MLA_LDS uint8_t* lds, int bid) {
+  // W^UK_i slice (128 rows x 128 cols bf16), then two 64-row blocks of query rows
+  MLA_LDS uint8_t* qbuf = lds + kNope * 256;
+  uint16_t* q_lat = (uint16_t*)(ws + Lw.off_qlat);
+
+  // (head, 128-column block of the latent): the four blocks of a head take ids 8 apart, so
+  // they run on one XCD and share its L2 for the head's query rows
+  const int full = (n_heads / 8) * 32;
+  int h, cb;
+  if (bid < full) {
+    h = 8 * (bid / 32) + bid % 8;
+    cb = (bid / 8) % 4;
+  } else {
+    h = (n_heads / 8) * 8 + (bid - full) / 4;
+    cb = (bid - full) % 4;
+  }
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int M = batch * sq;
+  const int nmb = (M + 63) / 64;      // 64-row blocks of query rows
+
+  // stage the slice: LDS row d holds columns cb*128 .. +127 of W^UK row 128 h + d,
+  // its 16-byte chunk k at chunk k ^ swz(d)
+  {
+    const uint8_t* gbase = (const uint8_t*)w_uk + ((size_t)h * kNope * kLat + cb * 128) * 2;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int P = 64 * (wave + 4 * k) + lane;   // 16-byte chunk index inside the 32 KB slice
+      int d = P >> 4;
+      int c = (P & 15) ^ swz(d);
+      const uint8_t* src = gbase + (size_t)d * (kLat * 2) + c * 16;
+      uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + (wave + 4 * k) * 1024));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
+    }
+  }
+  // copy query-row block mb into buffer (mb & 1): LDS chunk P = 64 (wave + 4 k) + lane holds
+  // row P / 16 of the block, physical chunk P % 16 = logical chunk ^ (row % 16); rows past
+  // M re-read row M - 1
+  auto stage_q = [&](int mb) {
+    MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int P = 64 * (wave + 4 * k) + lane;
+      const int r = P >> 4;
+      int m = mb * 64 + r;
+      m = m < M ? m : M - 1;
+      const int c = (P & 15) ^ (r & 15);
+      const uint16_t* src = q_nope + ((size_t)m * n_heads + h) * kNope + 8 * c;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qb + (wave + 4 * k) * 1024));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
+    }
+  };
+  stage_q(0);
+  // the rotary half of the latent query: q^R times a power of two (exact)
+  if (cb == 0) {
+    for (int i = tid; i < M * (kRope / 8); i += 256) {
+      int m = i / (kRope / 8), j = i % (kRope / 8);
+      const u32x4 v = *(const u32x4*)(q_rope + ((size_t)m * n_heads + h) * kRope + 8 * j);
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf2(bf2f((uint16_t)(v[e] & 0xffffu)) * qscale, bf2f((uint16_t)(v[e] >> 16)) * qscale);
+      *(u32x4*)(q_lat + ((size_t)m * n_heads + h) * kRow + kLat + 8 * j) = o;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  // B operand (K = d, N = column): lane 16 g + 4 e + q reads row d = 16 ks + 8 hh + 4 r + e,
+  // columns 32 wave + 16 (g % 2) + 4 q .. +3, which the transpose hands out as
+  // 4 consecutive d of column 32 wave + (lane % 32).
+  const int hh = lane >> 5;
+  const int n = lane & 31;
+  const int g16 = lane >> 4;
+  const int e_ = (lane >> 2) & 3;
+  const int q_ = lane & 3;
+  const int chunk = 4 * wave + 2 * (g16 & 1) + (q_ >> 1);
+  u32x4 bop[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x2 part[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      int d = 16 * ks + 8 * hh + 4 * r + e_;
+      int phys = (chunk & ~7) | ((chunk & 7) ^ (2 * e_ + r));
+      const MLA_LDS uint8_t* p = lds + d * 256 + phys * 16 + 8 * (q_ & 1);
+      s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
+      part[r] = __builtin_bit_cast(u32x2, v);
+    }
+    bop[ks] = u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
+  }
+
+  for (int mb = 0; mb < nmb; ++mb) {
+    if (mb + 1 < nmb) stage_q(mb + 1);   // the next block lands while this one is multiplied
+    const MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // A operand: lane reads query row 32 half + n of the block, d = 16 ks + 8 hh .. +7
+      const int r = 32 * half + n;
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 a = *(const MLA_LDS u32x4*)(qb + r * (kNope * 2) + (((2 * ks + hh) ^ (r & 15)) * 16));
+        // operands in swapped roles: the product is D^T, [column x query row]
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(a), acc, 0, 0, 0);
+      }
+      // D^T: lane holds query row 32 half + n, columns 32 wave + 8 (i/4) + 4 hh + i % 4, so
+      // each group of four registers is four adjacent columns: one 8-byte store
+      const int mm = mb * 64 + 32 * half + n;
+      if (mm < M) {
+        uint16_t* dst = q_lat + ((size_t)mm * n_heads + h) * kRow + cb * 128 + 32 * wave + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale),
+                                          pack_bf2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale)};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // next block landed (and this block's stores issued)
+    __syncthreads();                              // ... for every wave; this block's buffer is free
+  }
+}
+
+}  // namespace prep
+}  // namespace mla

@@ -29,7 +29,8 @@ EXPORTS = ("mla_status_str", "mla_cache_bytes", "mla_cache_append", "mla_cache_a
            "mla_q_project", "mla_decode_workspace_bytes", "mla_decode", "mla_decode_prepare", "mla_decode_attend",
            "mla_decode_finish", "mla_prefill_workspace_bytes", "mla_prefill", "mla_prefill_expand",
            "mla_prefill_attend", "mla_layer_workspace_bytes", "mla_q_compress", "mla_out_project",
-           "mla_decode_noalloc")
+           "mla_decode_noalloc", "mla_decode_step_workspace_bytes", "mla_decode_step")
+MLA_PHASE_PREPARE, MLA_PHASE_ATTEND, MLA_PHASE_FINISH, MLA_PHASE_ALL = 1, 2, 4, 7
 MLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 if not os.path.exists(LIB_PATH):
@@ -56,6 +57,14 @@ class MlaDims(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
+
+
+class MlaStepArgs(ctypes.Structure):
+    _fields_ = [("h", _P), ("w_dkv", _P), ("w_kr", _P), ("positions", _P), ("q_nope", _P), ("q_rope", _P),
+                ("w_uk", _P), ("w_uv", _P), ("cache", _P), ("num_blocks", _I), ("block_table", _P),
+                ("max_blocks", _I), ("seq_lens", _P), ("batch", _I), ("sq", _I), ("softmax_scale", ctypes.c_float),
+                ("num_splits", _I), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t), ("out", _P),
+                ("lse", _P), ("status", _P)]
 _lib.mla_status_str.restype = ctypes.c_char_p
 _lib.mla_status_str.argtypes = [ctypes.c_int]
 _lib.mla_cache_bytes.restype = ctypes.c_size_t
@@ -88,6 +97,10 @@ for _name in ("mla_decode", "mla_decode_prepare", "mla_decode_attend", "mla_deco
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
                                      ctypes.c_float, _I, _P, ctypes.c_size_t, _P, _P, _P, _P]
+_lib.mla_decode_step_workspace_bytes.restype = ctypes.c_size_t
+_lib.mla_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(MlaDims), _I, _I, _I]
+_lib.mla_decode_step.restype = ctypes.c_int
+_lib.mla_decode_step.argtypes = [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaStepArgs), _I, _P]
 _lib.mla_decode_noalloc.restype = ctypes.c_int
 _lib.mla_decode_noalloc.argtypes = [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
                                     ctypes.c_float, _I, _P, _P, _P, _P]
@@ -230,6 +243,36 @@ def mla_decode(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_l
     ``workspace`` is a byte tensor of at least mla_decode_workspace_bytes(d, batch, sq, num_splits)."""
     _decode_call("mla_decode", d, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale,
                  workspace, out, lse, status, num_splits, stream)
+
+
+def mla_decode_step_workspace_bytes(d: MlaDims, batch: int, sq: int, num_splits: int = 0) -> int:
+    return int(_lib.mla_decode_step_workspace_bytes(ctypes.byref(d), batch, sq, num_splits))
+
+
+def prepared_decode_step(d: MlaDims, h, w_dkv, w_kr, positions, q_nope, q_rope, w_uk, w_uv, cache, block_table,
+                         seq_lens, softmax_scale: float, workspace, out, lse=None, status=None, num_splits: int = 0,
+                         phases: int = MLA_PHASE_ALL, stream=None):
+    """A decode step that appends its own sq tokens per sequence (mla_cache_append with t = sq, then
+    mla_decode): arguments marshalled once into an mla_step_args; returns a zero-argument launcher of
+    the given phases that keeps references to the tensors."""
+    keep = (d, h, w_dkv, w_kr, positions, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, workspace, out,
+            lse, status)
+    a = MlaStepArgs(_ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(positions), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                    _ptr(w_uv), _ptr(cache), int(cache.shape[0]), _ptr(block_table), int(block_table.shape[1]),
+                    _ptr(seq_lens), int(q_nope.shape[0]), int(q_nope.shape[1]), float(softmax_scale), num_splits,
+                    _ptr(workspace), _nbytes(workspace), _ptr(out), _ptr(lse), _ptr(status))
+    args = (ctypes.byref(d), ctypes.byref(a), phases, _stream(stream))
+
+    def launch(_keep=keep, _a=a) -> None:
+        _check("mla_decode_step", _lib.mla_decode_step(*args))
+    return launch
+
+
+def mla_decode_step(d: MlaDims, h, w_dkv, w_kr, positions, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens,
+                    softmax_scale: float, workspace, out, lse=None, status=None, num_splits: int = 0,
+                    phases: int = MLA_PHASE_ALL, stream=None) -> None:
+    prepared_decode_step(d, h, w_dkv, w_kr, positions, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens,
+                         softmax_scale, workspace, out, lse, status, num_splits, phases, stream)()
 
 
 def mla_decode_noalloc(d: MlaDims, q_nope, q_rope, w_uk, w_uv, cache, block_table, seq_lens, softmax_scale: float,

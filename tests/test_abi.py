@@ -352,3 +352,38 @@ def test_noalloc_decode_rejects_before_any_device_call():
     assert "scratch" in mla.mla_status_str(-9)
     # the decode benchmark's shape fits (batch 64, 128 heads, one query token, 256 ranges)
     assert mla.mla_decode_workspace_bytes(v2, 64, 1, 256) <= mla.MLA_NOALLOC_SCRATCH_BYTES
+
+
+def test_decode_step_rejects_before_any_launch():
+    """mla_decode_step checks the append's and decode's arguments and its workspace on the host
+    before anything is launched (these calls run without a GPU)."""
+    lib = mla.raw_library()
+    v2 = mla.dims(128, 128, 64, 512, 5120)
+    n = mla.mla_decode_step_workspace_bytes(v2, 2, 1, 8)
+    assert n >= mla.mla_decode_workspace_bytes(v2, 2, 1, 8) + mla.mla_cache_append_workspace_bytes(v2, 2, 1)
+    assert mla.mla_decode_step_workspace_bytes(mla.dims(128, 128, 64, 512, 5120, dtype="bf16_fp8"), 2, 1, 8) == 0
+    assert mla.mla_decode_step_workspace_bytes(v2, 2, 9, 8) == 0
+
+    def args(**kw):
+        f = dict(h=FAKE, w_dkv=FAKE, w_kr=FAKE, positions=FAKE, q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE,
+                 cache=FAKE, num_blocks=64, block_table=FAKE, max_blocks=16, seq_lens=FAKE, batch=2, sq=1,
+                 softmax_scale=0.07, num_splits=8, workspace=FAKE, workspace_bytes=n, out=FAKE, lse=None, status=None)
+        f.update(kw)
+        return mla.MlaStepArgs(**f)
+
+    def call(a, d=v2, phases=7):
+        return lib.mla_decode_step(ctypes.byref(d), ctypes.byref(a), phases, None)
+
+    assert lib.mla_decode_step(ctypes.byref(v2), None, 7, None) == -1
+    assert call(args(h=None)) == -1
+    assert call(args(q_nope=None)) == -1
+    assert call(args(workspace=None)) == -1
+    assert call(args(), phases=0) == -2 and call(args(), phases=8) == -2
+    assert call(args(sq=0)) == -2
+    assert call(args(sq=9)) == -6
+    assert call(args(h=FAKE + 4)) == -4
+    assert call(args(out=FAKE + 4)) == -4
+    assert call(args(workspace=FAKE + 128)) == -4
+    assert call(args(workspace_bytes=n - 1)) == -5
+    assert call(args(), d=mla.dims(128, 128, 64, 512, 5120, dtype="bf16_fp8")) == -8
+    assert call(args(), d=mla.dims(8, 16, 8, 32, 64, dtype="f32")) == -8
