@@ -62,7 +62,8 @@ def sources_sha256(sources) -> str:
 def measured_counters(workload: str) -> dict:
     """Figures per attention launch from the committed counter profile of this workload:
     ``traffic`` (HBM bytes, FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's reading) and
-    ``mfma_busy`` (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 4 SIMDs x CUs).  Empty when
+    ``mfma_busy`` (rocprofv3's MfmaUtil / 100: SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs, over
+    the largest GRBM_GUI_ACTIVE times the SIMD count; mean of the timed dispatches).  Empty when
     there is no profile or the attention sources changed since the counters were taken."""
     if workload not in COUNTER_PROFILES:
         return {}

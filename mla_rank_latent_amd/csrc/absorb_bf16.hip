@@ -25,7 +25,7 @@
 
 namespace mla {
 
-__global__ __launch_bounds__(256) void absorb_bf16_kernel(const uint16_t* __restrict__ q_nope,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void absorb_bf16_kernel(const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           const int32_t* __restrict__ seq_lens, int max_blocks,

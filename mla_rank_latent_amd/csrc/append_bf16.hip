@@ -145,16 +145,29 @@ __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __
                                                                  int max_blocks, uint16_t* __restrict__ cache,
                                                                  int num_blocks, int tokens, int t_per_seq,
                                                                  double rope_base, int32_t* status) {
-  // thread = (token, pair of adjacent columns): a RoPE pair for the k^R part
+  // thread = (token, pair of adjacent columns): a RoPE pair for the k^R part.  The
+  // position, then the first sixteen slices, are loaded first; the block-table lookup
+  // (which needs the position) and the rotation angle are worked out while the slices land.
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)tokens * (kRow / 2)) return;
   const int tok = (int)(idx / (kRow / 2));
   const int col = 2 * (int)(idx % (kRow / 2));
   const float* pp = part + (size_t)tok * nslice * kRow + col;
+  const int pos = positions[tok];
+  float2 p[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) p[u] = *(const float2*)(pp + (size_t)(u < nslice ? u : 0) * kRow);
+  uint16_t* dst = append_dst(cache, block_table, max_blocks, num_blocks, tok, t_per_seq, pos, status);
+  double sn = 0.0, cs = 1.0;
+  if (col >= kLat) rope_angle(pos, (col - kLat) >> 1, kRope, rope_base, &sn, &cs);
   float v0 = 0.0f, v1 = 0.0f;
-  const int pos = positions[tok];   // issued with the partial sums: one memory round trip
-  for (int s0 = 0; s0 < nslice; s0 += 16) {
-    float2 p[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (u < nslice) {
+      v0 += p[u].x;
+      v1 += p[u].y;
+    }
+  for (int s0 = 16; s0 < nslice; s0 += 16) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) p[u] = *(const float2*)(pp + (size_t)(s0 + u < nslice ? s0 + u : s0) * kRow);
 #pragma unroll
@@ -164,14 +177,12 @@ __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __
         v1 += p[u].y;
       }
   }
-  uint16_t* dst = append_dst(cache, block_table, max_blocks, num_blocks, tok, t_per_seq, pos, status);
   if (dst == nullptr) return;
   uint32_t outv;
   if (col < kLat) {
     outv = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
   } else {
-    double y0, y1;
-    rope_pair((double)v0, (double)v1, pos, (col - kLat) >> 1, kRope, rope_base, &y0, &y1);
+    const double y0 = (double)v0 * cs - (double)v1 * sn, y1 = (double)v0 * sn + (double)v1 * cs;
     outv = (uint32_t)d2bf(y0) | ((uint32_t)d2bf(y1) << 16);
   }
   *(uint32_t*)(dst + col) = outv;

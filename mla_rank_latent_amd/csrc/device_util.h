@@ -149,11 +149,14 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
 }
 
 // RoPE on one pair at position pos: angle pos * base^(-2i/d), evaluated in fp64.
+__device__ __forceinline__ void rope_angle(int pos, int i, int d, double base, double* s, double* c) {
+  double theta = pow(base, -2.0 * (double)i / (double)d);
+  sincos((double)pos * theta, s, c);
+}
 __device__ __forceinline__ void rope_pair(double x0, double x1, int pos, int i, int d, double base,
                                           double* y0, double* y1) {
-  double theta = pow(base, -2.0 * (double)i / (double)d);
   double s, c;
-  sincos((double)pos * theta, &s, &c);
+  rope_angle(pos, i, d, base, &s, &c);
   *y0 = x0 * c - x1 * s;
   *y1 = x0 * s + x1 * c;
 }

@@ -14,13 +14,15 @@ __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf
 // ---- split append: K slices of at most kSliceSteps k-steps (32 elements) of d_model
 constexpr int kSliceSteps = 10;
 constexpr int kSliceChunks = 4 * kSliceSteps + 1;  // 16-byte chunks per padded LDS row
-constexpr int kTileRows = 64 + 32;                 // tokens + weight rows of one tile
-constexpr int kAppendPartialLds = (kTileRows * kSliceChunks + 63) / 64 * 1024;
+constexpr int kAppendPartialLds = (32 * kSliceChunks + 63) / 64 * 1024;   // 32 weight rows
 
 // One [64 tokens x 32 columns] partial product over K slice sl of the split append:
 // ct = 32-column tile of the 576-wide row, tg = 64-token group; lds holds
 // kAppendPartialLds bytes (whole 1 KB copies: the lanes of the last copy past the tile
-// still write their 16 bytes).
+// still write their 16 bytes).  The 32 weight rows of the tile, read by all four waves,
+// go through LDS; each wave's 16 token rows go straight into its operand registers
+// (lane: token 16 wave + lane % 16, features 32 ks + 8 (lane / 16) .. +7 of the slice,
+// the MFMA 16x16x32 A layout), issued together with the weight copies.
 __device__ __forceinline__ void append_partial_tile(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
                                                     const uint16_t* __restrict__ w_kr, int tokens, int d_model,
                                                     int nslice, float* __restrict__ part, MLA_LDS uint8_t* lds, int ct,
@@ -32,23 +34,25 @@ __device__ __forceinline__ void append_partial_tile(const uint16_t* __restrict__
   const int nsteps = k1 - k0;                       // 1 .. kSliceSteps
   const int rch = 4 * nsteps + 1;                   // chunks per padded LDS row (odd)
 
-  // copy: LDS chunk P = 64 q + lane holds row P / rch, chunk P % rch (the last chunk of a
-  // row is padding: it re-reads the row's first chunk)
-  const int nchunks = kTileRows * rch;
+  const int tok = tg * 64 + wave * 16 + (lane & 15);
+  const bool tok_ok = tok < tokens;
+  const uint16_t* hrow = h + (size_t)(tok_ok ? tok : 0) * d_model + 32 * k0 + 8 * (lane >> 4);
+  u32x4 a[kSliceSteps];
+#pragma unroll
+  for (int ks = 0; ks < kSliceSteps; ++ks)
+    if (ks < nsteps) a[ks] = *(const u32x4*)(hrow + 32 * ks);
+
+  // copy: LDS chunk P = 64 q + lane holds weight row P / rch, chunk P % rch (the last chunk
+  // of a row is padding: it re-reads the row's first chunk)
+  const int nchunks = 32 * rch;
   for (int q = wave; q * 64 < nchunks; q += 4) {
     int P = q * 64 + lane;
     if (P >= nchunks) P = nchunks - 1;              // the tail lanes repeat the last chunk
     const int row = P / rch;
     int ch = P - row * rch;
     if (ch == rch - 1) ch = 0;
-    const uint16_t* src;
-    if (row < 64) {
-      const int tok = tg * 64 + row;
-      src = h + (size_t)(tok < tokens ? tok : 0) * d_model;
-    } else {
-      const int col = ct * 32 + (row - 64);
-      src = col < kLat ? w_dkv + (size_t)col * d_model : w_kr + (size_t)(col - kLat) * d_model;
-    }
+    const int col = ct * 32 + row;
+    const uint16_t* src = col < kLat ? w_dkv + (size_t)col * d_model : w_kr + (size_t)(col - kLat) * d_model;
     src += 32 * k0 + 8 * ch;
     const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + q * 1024));
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
@@ -57,18 +61,18 @@ __device__ __forceinline__ void append_partial_tile(const uint16_t* __restrict__
   __syncthreads();
 
   // wave w: tokens 16 w .. +15 (A rows) against the 32 columns (two 16-wide B blocks)
-  const bool tok_ok = tg * 64 + wave * 16 + (lane & 15) < tokens;
-  const MLA_LDS uint8_t* arow = lds + (wave * 16 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
-  const MLA_LDS uint8_t* brow0 = lds + (64 + (lane & 15)) * rch * 16 + 16 * (lane >> 4);
+  const MLA_LDS uint8_t* brow0 = lds + (lane & 15) * rch * 16 + 16 * (lane >> 4);
   const MLA_LDS uint8_t* brow1 = brow0 + 16 * rch * 16;
   f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int ks = 0; ks < nsteps; ++ks) {
-    u32x4 a = *(const MLA_LDS u32x4*)(arow + 64 * ks);
-    const u32x4 b0 = *(const MLA_LDS u32x4*)(brow0 + 64 * ks);
-    const u32x4 b1 = *(const MLA_LDS u32x4*)(brow1 + 64 * ks);
-    if (!tok_ok) a = u32x4{0u, 0u, 0u, 0u};
-    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b0), acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b1), acc[1], 0, 0, 0);
+#pragma unroll
+  for (int ks = 0; ks < kSliceSteps; ++ks) {
+    if (ks < nsteps) {
+      const u32x4 b0 = *(const MLA_LDS u32x4*)(brow0 + 64 * ks);
+      const u32x4 b1 = *(const MLA_LDS u32x4*)(brow1 + 64 * ks);
+      const u32x4 av = tok_ok ? a[ks] : u32x4{0u, 0u, 0u, 0u};
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), as_bf8(b0), acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(av), as_bf8(b1), acc[1], 0, 0, 0);
+    }
   }
   // D: lane holds column lane % 16 of its 16-column block, tokens 4 (lane / 16) + r of the wave's 16
 #pragma unroll
@@ -81,17 +85,18 @@ __device__ __forceinline__ void append_partial_tile(const uint16_t* __restrict__
 }
 
 // ---- absorbed queries
-constexpr int kAbsorbLds = kNope * 256 + 2 * 64 * kNope * 2;
+constexpr int kAbsorbLds = kNope * 256;   // the 128 x 128 W^UK slice
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
 // One (head, 128 latent columns) block of the absorbed queries; bid = 0 .. 4 n_heads - 1;
-// lds holds kAbsorbLds bytes, 1 KB aligned.
+// lds holds kAbsorbLds bytes, 1 KB aligned.  The weight slice goes through LDS (its
+// contraction index runs along strided rows, which the transposing LDS read turns into
+// the MFMA operand); the query rows, contiguous along the contraction, go straight into
+// operand registers.
 __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
                                             const uint16_t* __restrict__ w_uk, int batch, int sq, int n_heads,
                                             float qscale, uint8_t* __restrict__ ws, const WsLayout& Lw,
                                             MLA_LDS uint8_t* lds, int bid) {
-  // W^UK_i slice (128 rows x 128 cols bf16), then two 64-row blocks of query rows
-  MLA_LDS uint8_t* qbuf = lds + kNope * 256;
   uint16_t* q_lat = (uint16_t*)(ws + Lw.off_qlat);
 
   // (head, 128-column block of the latent): the four blocks of a head take ids 8 apart, so
@@ -109,7 +114,22 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int M = batch * sq;
-  const int nmb = (M + 63) / 64;      // 64-row blocks of query rows
+  const int nmb = (M + 31) / 32;      // 32-row blocks of query rows
+  const int hh = lane >> 5;
+  const int n = lane & 31;
+
+  // query operand of row block mb (MFMA 32x32x16 layout, the query rows on the N side):
+  // lane (hh, n) holds row 32 mb + n, features 16 ks + 8 hh .. +7; rows past M re-read row M - 1
+  auto load_q = [&](int mb, u32x4 (&qa)[8]) {
+    int m = mb * 32 + n;
+    m = m < M ? m : M - 1;
+    const uint16_t* src = q_nope + ((size_t)m * n_heads + h) * kNope + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qa[ks] = *(const u32x4*)(src + 16 * ks);
+  };
+  u32x4 qa[2][8];
+  load_q(0, qa[0]);
+  if (nmb > 1) load_q(1, qa[1]);
 
   // stage the slice: LDS row d holds columns cb*128 .. +127 of W^UK row 128 h + d,
   // its 16-byte chunk k at chunk k ^ swz(d)
@@ -125,24 +145,6 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
       asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
     }
   }
-  // copy query-row block mb into buffer (mb & 1): LDS chunk P = 64 (wave + 4 k) + lane holds
-  // row P / 16 of the block, physical chunk P % 16 = logical chunk ^ (row % 16); rows past
-  // M re-read row M - 1
-  auto stage_q = [&](int mb) {
-    MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int P = 64 * (wave + 4 * k) + lane;
-      const int r = P >> 4;
-      int m = mb * 64 + r;
-      m = m < M ? m : M - 1;
-      const int c = (P & 15) ^ (r & 15);
-      const uint16_t* src = q_nope + ((size_t)m * n_heads + h) * kNope + 8 * c;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qb + (wave + 4 * k) * 1024));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory");
-    }
-  };
-  stage_q(0);
   // the rotary half of the latent query: q^R times a power of two (exact)
   if (cb == 0) {
     for (int i = tid; i < M * (kRope / 8); i += 256) {
@@ -161,8 +163,6 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
   // B operand (K = d, N = column): lane 16 g + 4 e + q reads row d = 16 ks + 8 hh + 4 r + e,
   // columns 32 wave + 16 (g % 2) + 4 q .. +3, which the transpose hands out as
   // 4 consecutive d of column 32 wave + (lane % 32).
-  const int hh = lane >> 5;
-  const int n = lane & 31;
   const int g16 = lane >> 4;
   const int e_ = (lane >> 2) & 3;
   const int q_ = lane & 3;
@@ -182,35 +182,30 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
     bop[ks] = u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
   }
 
-  for (int mb = 0; mb < nmb; ++mb) {
-    if (mb + 1 < nmb) stage_q(mb + 1);   // the next block lands while this one is multiplied
-    const MLA_LDS uint8_t* qb = qbuf + (mb & 1) * (64 * kNope * 2);
+  // row blocks two at a time in flight: block mb multiplies while block mb + 1 lands
+  auto do_block = [&](int mb, u32x4(&cur)[8]) {
+    f32x16 acc;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // A operand: lane reads query row 32 half + n of the block, d = 16 ks + 8 hh .. +7
-      const int r = 32 * half + n;
-      f32x16 acc;
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int ks = 0; ks < 8; ++ks)
+      // operands in swapped roles: the product is D^T, [column x query row]
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(cur[ks]), acc, 0, 0, 0);
+    if (mb + 2 < nmb) load_q(mb + 2, cur);
+    // D^T: lane holds query row 32 mb + n, columns 32 wave + 8 (i/4) + 4 hh + i % 4, so
+    // each group of four registers is four adjacent columns: one 8-byte store
+    const int mm = mb * 32 + n;
+    if (mm < M) {
+      uint16_t* dst = q_lat + ((size_t)mm * n_heads + h) * kRow + cb * 128 + 32 * wave + 4 * hh;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 a = *(const MLA_LDS u32x4*)(qb + r * (kNope * 2) + (((2 * ks + hh) ^ (r & 15)) * 16));
-        // operands in swapped roles: the product is D^T, [column x query row]
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(a), acc, 0, 0, 0);
-      }
-      // D^T: lane holds query row 32 half + n, columns 32 wave + 8 (i/4) + 4 hh + i % 4, so
-      // each group of four registers is four adjacent columns: one 8-byte store
-      const int mm = mb * 64 + 32 * half + n;
-      if (mm < M) {
-        uint16_t* dst = q_lat + ((size_t)mm * n_heads + h) * kRow + cb * 128 + 32 * wave + 4 * hh;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale),
-                                          pack_bf2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale)};
-      }
+      for (int g = 0; g < 4; ++g)
+        *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale),
+                                        pack_bf2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale)};
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // next block landed (and this block's stores issued)
-    __syncthreads();                              // ... for every wave; this block's buffer is free
+  };
+  for (int mb = 0; mb < nmb; mb += 2) {
+    do_block(mb, qa[0]);
+    if (mb + 1 < nmb) do_block(mb + 1, qa[1]);
   }
 }
 

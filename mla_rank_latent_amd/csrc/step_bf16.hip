@@ -15,7 +15,7 @@
 
 namespace mla {
 
-__global__ __launch_bounds__(256) void step_prepare_bf16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void step_prepare_bf16_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv, const uint16_t* __restrict__ w_kr,
     int tokens, int d_model, int nslice, float* __restrict__ part, int n_app, const uint16_t* __restrict__ q_nope,
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ seq_lens,
