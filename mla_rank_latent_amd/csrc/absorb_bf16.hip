@@ -14,10 +14,10 @@
 // rows of W^UK (d_h), which are strided in memory; the LDS transpose read
 // (ds_read_b64_tr_b16) turns the row-major slice into the K-contiguous
 // operand the MFMA needs.  The query rows of the head (256 bytes each, one
-// row per n_heads * 256 bytes in memory) reach LDS in double-buffered blocks
-// of 64 by direct-to-LDS copies that read four whole rows each; their 16-byte
-// chunks are XOR-swizzled by row so the operand reads are free of bank
-// conflicts.
+// row per n_heads * 256 bytes in memory) are contiguous along the contraction,
+// so each lane loads its operand's eight features straight into registers,
+// two 32-row blocks in flight at a time.  The slice (32 KB) is the only LDS:
+// four workgroups fit on a CU.
 //
 // The first workgroup of the grid builds the split plan for the attention
 // kernel (the two are independent, so the plan costs no extra launch).
