@@ -112,7 +112,8 @@ bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L
   L->off_seg = off;   off += up((size_t)(batch + 1) * 4);
   L->off_piece = off; off += up((size_t)(batch + 1) * 4);
   L->off_wgseg = off; off += up((size_t)W * 4);
-  L->off_qlat = off;  off += up((size_t)batch * sq * d->n_heads * R * elem_size(d->dtype));
+  const size_t qrows = (size_t)batch * sq * d->n_heads;
+  L->off_qlat = off;  off += up((bf ? qlat_padded_rows(qrows) : qrows) * R * elem_size(d->dtype));
   L->off_lse = off;   off += up((size_t)L->G * L->P * L->rows * 8);
   // partial latent sums: bf16 for the bf16 kernels, fp32 for the fp32 ones
   L->off_o = off;     off += up((size_t)L->G * L->P * L->rows * d->d_latent * (bf ? 2 : 4));

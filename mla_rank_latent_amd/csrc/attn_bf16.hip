@@ -107,12 +107,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   const int n = lane & 31;     // row within the wave's 32 (MFMA column)
   const int hh = lane >> 5;    // lane half
 
-  // XCD-aware order: block ids that differ by a multiple of 8 share an XCD (and
-  // its L2); the G head groups of one token range take ids 8 apart.
+  // XCD-aware order: block ids equal modulo 8 share an XCD (and its L2).  The G head
+  // groups of a token range run on one XCD, so the range's cache rows leave HBM once.
+  // With W a multiple of 8, XCD x also takes the consecutive ranges x W/8 .. +W/8-1, so
+  // the ranges of one sequence share its absorbed queries in L2; otherwise ranges go to
+  // the XCDs in turn.
   const int G = Lw.G;
   const int bid = blockIdx.x;
-  const int w = (bid / (8 * G)) * 8 + (bid % 8);
-  const int g = (bid / 8) % G;
+  int w, g;
+  if (W % 8 == 0) {
+    const int j = bid / 8;
+    g = j % G;
+    w = (bid % 8) * (W / 8) + j / G;
+  } else {
+    w = (bid / (8 * G)) * 8 + (bid % 8);
+    g = (bid / 8) % G;
+  }
   if (w >= W) return;
 
   const MLA_CONST PlanHeader* hdr = as_const((const PlanHeader*)(ws + Lw.off_hdr));
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
   const MLA_CONST int32_t* wgseg = as_const((const int32_t*)(ws + Lw.off_wgseg));
   const MLA_CONST int32_t* lens = as_const(seq_lens);
   const MLA_CONST int32_t* btab = as_const(block_table);
-  const uint16_t* q_lat = (const uint16_t*)(ws + Lw.off_qlat);
+  const uint8_t* q_lat = ws + Lw.off_qlat;   // absorbed queries in operand order (qlat_byte)
   float2* part_ml = (float2*)(ws + Lw.off_lse);
   uint16_t* part_o = (uint16_t*)(ws + Lw.off_o);   // bf16
 
@@ -233,11 +243,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     const int tok_end = e < L ? e : L;
     const int lim = L - sq + s_idx;   // query s sees tokens j <= L - sq + s
 
+    const int nsub = tok_end > a ? (tok_end - a + kSubTok - 1) / kSubTok : 0;
+    // block ids of the first three stages: scalar loads issued ahead of the query loads
+    const int blk0 = 0 < nsub ? lookup_block(b, a) : 0;
+    const int blk1 = 1 < nsub ? lookup_block(b, a + kSubTok) : 0;
+    int blk_next = 2 < nsub ? lookup_block(b, a + 2 * kSubTok) : 0;
     {
-      const uint16_t* qp = q_lat + ((size_t)(b * sq + s_idx) * n_heads + (row_ok ? head : 0)) * kRow + 8 * hh;
+      // row r of the absorbed queries (for a padding row, the sequence's row 0, zeroed):
+      // k-step ks of this lane's operand is the 16 bytes at qlat_byte(r, 16 ks + 8 hh), so
+      // each load of the wave is one 1 KB run
+      const size_t r = row_ok ? ((size_t)b * n_heads + head) * sq + s_idx : (size_t)b * n_heads * sq;
+      const uint8_t* qp = q_lat + qlat_byte(r, 8 * hh);
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
-        const u32x4 v = *(const u32x4*)(qp + 16 * ks);
+        const u32x4 v = *(const u32x4*)(qp + 1024 * ks);
         qreg[ks] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
@@ -251,7 +270,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
-    const int nsub = tok_end > a ? (tok_end - a + kSubTok - 1) / kSubTok : 0;
     auto tlast_of = [&](int k) {
       const int t = tok_end - 1 - (a + k * kSubTok);
       return t < kSubTok - 1 ? t : kSubTok - 1;
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     for (int k = 0; k < 2; ++k) {
       set_ld_off(k < nsub ? tlast_of(k) : kSubTok - 1);
       if (k < nsub) {
-        issue_stage(k, stage_base(lookup_block(b, a + k * kSubTok), a + k * kSubTok));
+        issue_stage(k, stage_base(k == 0 ? blk0 : blk1, a + k * kSubTok));
       } else {
         const uint32_t idle_dst = (uint32_t)(uintptr_t)(lds + k * kStageBytes + wave * 1024);
 #pragma unroll
@@ -270,9 +288,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(
     // the weights of the (empty) stage before the first: zero
     *(MLA_LDS u32x4*)(pbuf + kPBytes + wave * 2048 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     *(MLA_LDS u32x4*)(pbuf + kPBytes + wave * 2048 + 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-    // block ids are looked up one stage ahead of their copies, so that the
+    // later block ids are looked up one stage ahead of their copies, so that the
     // scalar load's latency is hidden behind a whole stage of work
-    int blk_next = 2 < nsub ? lookup_block(b, a + 2 * kSubTok) : 0;
 
     // Iteration it scores stage it and, interleaved with that stage's softmax,
     // runs the latent product of stage it - 1, so the softmax's vector work

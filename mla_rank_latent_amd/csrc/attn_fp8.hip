@@ -114,12 +114,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
   const int n = lane & 31;     // row within the wave's 32 (MFMA column)
   const int hh = lane >> 5;    // lane half
 
-  // XCD-aware order: block ids that differ by a multiple of 8 share an XCD (and
-  // its L2); the G head groups of one token range take ids 8 apart.
+  // XCD-aware order: block ids equal modulo 8 share an XCD (and its L2).  The G head
+  // groups of a token range run on one XCD, so the range's cache rows leave HBM once.
+  // With W a multiple of 8, XCD x also takes the consecutive ranges x W/8 .. +W/8-1, so
+  // the ranges of one sequence share its absorbed queries in L2; otherwise ranges go to
+  // the XCDs in turn.
   const int G = Lw.G;
   const int bid = blockIdx.x;
-  const int w = (bid / (8 * G)) * 8 + (bid % 8);
-  const int g = (bid / 8) % G;
+  int w, g;
+  if (W % 8 == 0) {
+    const int j = bid / 8;
+    g = j % G;
+    w = (bid % 8) * (W / 8) + j / G;
+  } else {
+    w = (bid / (8 * G)) * 8 + (bid % 8);
+    g = (bid / 8) % G;
+  }
   if (w >= W) return;
 
   const MLA_CONST PlanHeader* hdr = as_const((const PlanHeader*)(ws + Lw.off_hdr));
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
   const MLA_CONST int32_t* wgseg = as_const((const int32_t*)(ws + Lw.off_wgseg));
   const MLA_CONST int32_t* lens = as_const(seq_lens);
   const MLA_CONST int32_t* btab = as_const(block_table);
-  const uint16_t* q_lat = (const uint16_t*)(ws + Lw.off_qlat);
+  const uint8_t* q_lat = ws + Lw.off_qlat;   // absorbed queries in operand order (qlat_byte)
   float2* part_ml = (float2*)(ws + Lw.off_lse);
   uint16_t* part_o = (uint16_t*)(ws + Lw.off_o);   // bf16
 
@@ -262,11 +272,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
     {
       // code k-step ks < 32 takes features 32 (ks / 2) + 16 hh + 8 (ks % 2) .. +7; k^R k-step
       // 32 + k takes features 512 + 16 k + 8 hh .. +7
-      const uint16_t* qp = q_lat + ((size_t)(b * sq + s_idx) * n_heads + (row_ok ? head : 0)) * kRow;
+      // row r of the absorbed queries (for a padding row, the sequence's row 0, zeroed)
+      const size_t r = row_ok ? ((size_t)b * n_heads + head) * sq + s_idx : (size_t)b * n_heads * sq;
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
         const int f = ks < 32 ? 32 * (ks >> 1) + 16 * hh + 8 * (ks & 1) : 16 * ks + 8 * hh;
-        u32x4 v = *(const u32x4*)(qp + f);
+        u32x4 v = *(const u32x4*)(q_lat + qlat_byte(r, f));
         v = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
         if (ks < 32) qreg[ks] = v;
         else *(MLA_LDS u32x4*)(lds + (qr_off ^ (32 * (ks - 32)))) = v;

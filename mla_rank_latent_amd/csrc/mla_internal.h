@@ -31,6 +31,23 @@ constexpr int kFp8RopeOff = kBlk * kLat;                       // 32768
 constexpr int kFp8ScaleOff = kFp8RopeOff + kBlk * kRope * 2;   // 40960
 constexpr int kFp8PageBytes = kFp8ScaleOff + kBlk * 4;         // 41216
 
+// Absorbed queries of the bf16 kernels, in the order the attention kernels load them.
+// Query row r = (b n_heads + head) sq + s (a sequence's heads, each with its query
+// tokens); rows in blocks of 32; inside a block, 16-feature step ks (0..35) takes 1 KB,
+// in which lane 32 hh + (r % 32) holds features 16 ks + 8 hh .. +7 of row r: the
+// operand layout of MFMA 32x32x16 with the rows on its 32-wide side.  A wave that reads
+// 32 consecutive rows then loads whole 1 KB runs.
+constexpr int kQBlockRows = 32;
+constexpr size_t kQBlockBytes = (size_t)kQBlockRows * kRow * 2;   // 36864
+__host__ __device__ inline size_t qlat_padded_rows(size_t rows) {
+  return (rows + kQBlockRows - 1) / kQBlockRows * kQBlockRows;
+}
+// byte offset of feature f (0..575) of row r
+__host__ __device__ inline size_t qlat_byte(size_t r, int f) {
+  return (r / kQBlockRows) * kQBlockBytes + (size_t)(f >> 4) * 1024 +
+         (size_t)((((f >> 3) & 1) * kQBlockRows) + (int)(r % kQBlockRows)) * 16 + (size_t)(f & 7) * 2;
+}
+
 // f32 generic path limits
 constexpr int kF32MaxWidth = 1024;
 constexpr int kF32MaxSq = 64;

@@ -97,18 +97,29 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
                                             const uint16_t* __restrict__ w_uk, int batch, int sq, int n_heads,
                                             float qscale, uint8_t* __restrict__ ws, const WsLayout& Lw,
                                             MLA_LDS uint8_t* lds, int bid) {
-  uint16_t* q_lat = (uint16_t*)(ws + Lw.off_qlat);
+  uint8_t* q_lat = ws + Lw.off_qlat;   // operand order: qlat_byte()
 
-  // (head, 128-column block of the latent): the four blocks of a head take ids 8 apart, so
-  // they run on one XCD and share its L2 for the head's query rows
-  const int full = (n_heads / 8) * 32;
+  // (head, 128-column block of the latent).  Consecutive block ids go to the XCDs in turn,
+  // so ids equal modulo 8 share an XCD and its L2.  With n_heads a multiple of 64, XCD x
+  // takes heads 8 x .. 8 x + 7 (+ 64 k), all four column blocks of each: a head's blocks
+  // share its query rows in L2, and the 128-byte lines of the operand-order layout (16
+  // bytes of eight consecutive heads each) are written from one L2 only.  Otherwise the
+  // four blocks of a head take ids 8 apart.
   int h, cb;
-  if (bid < full) {
-    h = 8 * (bid / 32) + bid % 8;
-    cb = (bid / 8) % 4;
+  if (n_heads % 64 == 0) {
+    const int x = bid % 8, j = bid / 8;
+    const int lh = j / 4;
+    cb = j % 4;
+    h = 8 * x + lh % 8 + 64 * (lh / 8);
   } else {
-    h = (n_heads / 8) * 8 + (bid - full) / 4;
-    cb = (bid - full) % 4;
+    const int full = (n_heads / 8) * 32;
+    if (bid < full) {
+      h = 8 * (bid / 32) + bid % 8;
+      cb = (bid / 8) % 4;
+    } else {
+      h = (n_heads / 8) * 8 + (bid - full) / 4;
+      cb = (bid - full) % 4;
+    }
   }
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -154,7 +165,8 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         o[e] = pack_bf2(bf2f((uint16_t)(v[e] & 0xffffu)) * qscale, bf2f((uint16_t)(v[e] >> 16)) * qscale);
-      *(u32x4*)(q_lat + ((size_t)m * n_heads + h) * kRow + kLat + 8 * j) = o;
+      const size_t r = ((size_t)(m / sq) * n_heads + h) * sq + m % sq;
+      *(u32x4*)(q_lat + qlat_byte(r, kLat + 8 * j)) = o;
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -196,11 +208,15 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q_nope,
     // each group of four registers is four adjacent columns: one 8-byte store
     const int mm = mb * 32 + n;
     if (mm < M) {
-      uint16_t* dst = q_lat + ((size_t)mm * n_heads + h) * kRow + cb * 128 + 32 * wave + 4 * hh;
+      // features cb*128 + 32 wave + 8 g + 4 hh .. +3: half of one 16-byte operand unit
+      const size_t r = ((size_t)(mm / sq) * n_heads + h) * sq + mm % sq;
+      // f0 % 16 = 4 hh, so feature f0 + 8 g sits (g / 2) k-steps and (g % 2) lane halves on
+      uint8_t* dst = q_lat + qlat_byte(r, cb * 128 + 32 * wave + 4 * hh);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale),
-                                        pack_bf2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale)};
+        *(u32x2*)(dst + 1024 * (g >> 1) + 16 * kQBlockRows * (g & 1)) =
+            u32x2{pack_bf2(acc[4 * g] * qscale, acc[4 * g + 1] * qscale),
+                  pack_bf2(acc[4 * g + 2] * qscale, acc[4 * g + 3] * qscale)};
     }
   };
   for (int mb = 0; mb < nmb; mb += 2) {
