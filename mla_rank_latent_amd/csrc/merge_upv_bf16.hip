@@ -11,20 +11,22 @@
 // restores the head's output, out_i = W^UV_i o_lat (W^UV_i = rows 128 i ..
 // 128 i + 127 of W^UV, §2.1).
 //
-// One workgroup of eight waves per (head, 32 query rows).
+// One workgroup of eight waves per (head, 32 query rows), or two (each with half of the
+// head's output columns) when all query rows fit one block of 32.
 //  - Merge: sixteen threads per row, each owning 32 of its 512 columns
 //    (8 bytes at 128-byte strides, so the sixteen lanes of a row read whole
-//    128-byte blocks).  Two pieces' loads are in flight per thread and the
+//    128-byte blocks).  Up to four pieces' loads are in flight per thread and the
 //    piece weights are applied branch-free, so the partial states stream at
-//    memory rate instead of one round trip per piece.
+//    memory rate instead of one round trip per piece.  Rows with many pieces (small
+//    batches) split them over several thread slots, combined through LDS.
 //  - The merged latent goes to LDS as a bf16 high part and a bf16 remainder
 //    (two MFMAs per step keep the product close to fp32 accuracy).
-//  - Up-projection [32 x 512] . [512 x 128] on MFMA 32x32x16, computed
+//  - Up-projection [32 x 512] . [512 x columns] on MFMA 32x32x16, computed
 //    transposed so that each lane ends with four adjacent output columns per
-//    register group (8-byte stores): wave (kh, wc) takes output columns
-//    32 wc .. 32 wc + 31 over latent half kh, with its W^UV slice loaded into
-//    registers before the merge starts; the two latent halves are summed
-//    through LDS.
+//    register group (8-byte stores): each wave takes 32 output columns over one
+//    latent part (halves with 128 columns per workgroup, quarters with 64), with its
+//    W^UV slice loaded into registers before the merge starts; the parts are
+//    summed through LDS in part order.
 #include "device_util.h"
 
 namespace mla {
@@ -34,39 +36,51 @@ __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf
 constexpr int kMergeRows = 32;
 }  // namespace
 
+// NCS = workgroups per (head, row block), each taking 128 / NCS output columns: 1 when the
+// rows fill several blocks (the blocks of a head then share its W^UV slice in L2), 2 for a
+// single block (small batches), so that twice the workgroups each load half the slice.
+template <int NCS>
 __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __restrict__ w_uv, int batch, int sq,
                                                              int n_heads, int hg, int P,
                                                              const uint8_t* __restrict__ ws, WsLayout Lw,
                                                              uint16_t* __restrict__ out, float* __restrict__ lse) {
-  // hi and lo parts of the merged latent (32 rows x 512, swizzled 16-byte
-  // chunks), the upper latent half's partial products (32 x 128 fp32), and the
-  // slots' partial sums when rows are shared by several slots (32 x 512 fp32)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kMergeRows * kLat * 2 + kMergeRows * kNope * 4 +
-                                                         kMergeRows * kLat * 4];
+  // hi and lo parts of the merged latent (32 rows x 512, swizzled 16-byte chunks), then
+  // the slots' partial sums when rows are shared by several slots (32 x 512 fp32), whose
+  // space later takes the latent parts' partial products (up to 3 x 32 x 64 fp32)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kMergeRows * kLat * 2 + kMergeRows * kLat * 4];
   __shared__ float s_mx[kMergeRows], s_den[kMergeRows];
   MLA_LDS uint8_t* s_hi = (MLA_LDS uint8_t*)smem;
   MLA_LDS uint8_t* s_lo = s_hi + kMergeRows * kLat * 2;
-  MLA_LDS float* s_red = (MLA_LDS float*)(s_lo + kMergeRows * kLat * 2);
-  MLA_LDS uint8_t* s_comb = (MLA_LDS uint8_t*)(s_red + kMergeRows * kNope);
+  MLA_LDS uint8_t* s_comb = s_lo + kMergeRows * kLat * 2;
+  MLA_LDS float* s_red = (MLA_LDS float*)s_comb;
 
+  constexpr int kCols = kNope / NCS;        // output columns of the workgroup
+  constexpr int kWc = kCols / 32;           // 32-column blocks: 4 or 2
+  constexpr int kParts = 8 / kWc;           // latent parts: 2 or 4
+  constexpr int kSteps = kLat / kParts / 16;   // k-steps of 16 per part: 16 or 8
   const int M = batch * sq;
+  const int nmb = (M + kMergeRows - 1) / kMergeRows;
+  // the column parts of a (head, row block) take ids n_heads * nmb apart (one XCD when
+  // that is a multiple of 8), the row blocks of a head ids n_heads apart
   const int h = blockIdx.x % n_heads;
-  const int mb = blockIdx.x / n_heads;
+  const int mb = (blockIdx.x / n_heads) % nmb;
+  const int ch = blockIdx.x / (n_heads * nmb);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int n = lane & 31;
-  const int kh = wave >> 2;    // latent half of the up-projection
-  const int wc = wave & 3;     // output column block
+  const int kp = wave / kWc;    // latent part of the up-projection
+  const int wc = wave % kWc;    // output column block
+  const int col0 = ch * kCols + 32 * wc;
 
   // B operand (K = latent, N = output column): lane holds
-  // W^UV[128 h + 32 wc + n][256 kh + 16 ks + 8 hh .. +7], ks = 0..15.
-  u32x4 bop[16];
+  // W^UV[128 h + col0 + n][kLat / kParts * kp + 16 ks + 8 hh .. +7], ks = 0 .. kSteps - 1.
+  u32x4 bop[kSteps];
   {
-    const uint16_t* wp = w_uv + ((size_t)h * kNope + 32 * wc + n) * kLat + 256 * kh + 8 * hh;
+    const uint16_t* wp = w_uv + ((size_t)h * kNope + col0 + n) * kLat + (kLat / kParts) * kp + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) bop[ks] = *(const u32x4*)(wp + 16 * ks);
+    for (int ks = 0; ks < kSteps; ++ks) bop[ks] = *(const u32x4*)(wp + 16 * ks);
   }
 
   // ---- merge.  Sixteen threads (a slot) own one row's 512 columns: thread c16 of a slot
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
       }
     };
     auto put_lse = [&](int mm, float mx, float dn) {
-      if (lse != nullptr)
+      if (lse != nullptr && ch == 0)
         lse[(size_t)mm * n_heads + h] = dn > 0.0f ? (mx + __builtin_amdgcn_logf(dn)) * 0.69314718055994531f
                                                   : -__builtin_inff();
     };
@@ -219,13 +233,13 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
   }
   __syncthreads();
 
-  // ---- out[32 rows x 32 cols of this wave] over latent half kh
+  // ---- out[32 rows x 32 cols of this wave] over latent part kp
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const int chunk = 32 * kh + 2 * ks + hh;
+  for (int ks = 0; ks < kSteps; ++ks) {
+    const int chunk = (kLat / kParts / 8) * kp + 2 * ks + hh;
     const int off = n * (kLat * 2) + ((chunk & ~7) | ((chunk & 7) ^ (n & 7))) * 16;
     const u32x4 ah = *(const MLA_LDS u32x4*)(s_hi + off);
     const u32x4 al = *(const MLA_LDS u32x4*)(s_lo + off);
@@ -234,23 +248,26 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(bop[ks]), as_bf8(al), acc, 0, 0, 0);
   }
   // out^T layout: lane holds row n, register r column 32 wc + 8 (r / 4) + 4 hh + r % 4, so each
-  // group of four registers is four adjacent columns
-  if (kh == 1) {
+  // group of four registers is four adjacent columns.  Parts 1 .. kParts - 1 go through LDS
+  // (the combine's space is free again), part 0 adds them in part order and stores.
+  if (kp > 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      *(MLA_LDS f32x4*)(s_red + n * kNope + 32 * wc + 8 * g + 4 * hh) =
+      *(MLA_LDS f32x4*)(s_red + ((kp - 1) * kMergeRows + n) * kCols + 32 * wc + 8 * g + 4 * hh) =
           f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
   }
   __syncthreads();
-  if (kh == 0) {
+  if (kp == 0) {
     const int m = mb * kMergeRows + n;
     if (m < M) {
-      uint16_t* dst = out + ((size_t)m * n_heads + h) * kNope + 32 * wc + 4 * hh;
+      uint16_t* dst = out + ((size_t)m * n_heads + h) * kNope + col0 + 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 o = *(const MLA_LDS f32x4*)(s_red + n * kNope + 32 * wc + 8 * g + 4 * hh);
-        *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(acc[4 * g] + o[0], acc[4 * g + 1] + o[1]),
-                                        pack_bf2(acc[4 * g + 2] + o[2], acc[4 * g + 3] + o[3])};
+        f32x4 v = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+#pragma unroll
+        for (int q = 1; q < kParts; ++q)
+          v += *(const MLA_LDS f32x4*)(s_red + ((q - 1) * kMergeRows + n) * kCols + 32 * wc + 8 * g + 4 * hh);
+        *(u32x2*)(dst + 8 * g) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
       }
     }
   }
@@ -259,9 +276,14 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
 hipError_t launch_merge_upv_bf16(const WsLayout& L, const uint16_t* w_uv, int batch, int sq, int n_heads, uint8_t* ws,
                                  uint16_t* out, float* lse, hipStream_t st) {
   const int M = batch * sq;
-  dim3 grid(n_heads * ((M + kMergeRows - 1) / kMergeRows));
-  hipLaunchKernelGGL(merge_upv_bf16_kernel, grid, dim3(512), 0, st, w_uv, batch, sq, n_heads, L.hg, L.P,
-                     (const uint8_t*)ws, L, out, lse);
+  const int nmb = (M + kMergeRows - 1) / kMergeRows;
+  if (nmb == 1) {
+    hipLaunchKernelGGL(merge_upv_bf16_kernel<2>, dim3(n_heads * 2), dim3(512), 0, st, w_uv, batch, sq, n_heads, L.hg,
+                       L.P, (const uint8_t*)ws, L, out, lse);
+  } else {
+    hipLaunchKernelGGL(merge_upv_bf16_kernel<1>, dim3(n_heads * nmb), dim3(512), 0, st, w_uv, batch, sq, n_heads,
+                       L.hg, L.P, (const uint8_t*)ws, L, out, lse);
+  }
   return hipGetLastError();
 }
 
