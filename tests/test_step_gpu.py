@@ -3,8 +3,10 @@ products, the absorbed queries and the split plan in one launch) against
 mla_cache_append followed by mla_decode, through the C ABI: the written cache, out and
 lse must be equal bit for bit (the same kernels' code computes them), and the outputs
 match the oracle.  Covers one and two new tokens per sequence, ragged paged batches,
-the phases called one by one, the batch-64 context-8192 benchmark step, and a step of
-2048 new tokens (mla_cache_append's many-row GEMM path)."""
+the phases called one by one, two new tokens that fall in two token ranges, new
+positions inside the context rather than at its end and outside every table row
+(reported, not written), the batch-64 context-8192 benchmark step, and a step of 2048
+new tokens (mla_cache_append's many-row GEMM path)."""
 import numpy as np
 import pytest
 
@@ -14,27 +16,27 @@ from tests import harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _pair(x, phases_one_by_one=False):
+def _pair(x, phases_one_by_one=False, num_splits=0, status=0):
     import torch
     from mla_rank_latent_amd import mla
     spec = x["spec"]
     # reference: mla_cache_append (with its workspace) then mla_decode
-    r = H.GpuCase(x)
+    r = H.GpuCase(x, num_splits=num_splits)
     r.step()
     # the fused step on a fresh copy of the same inputs
-    c = H.GpuCase(x)
-    n = mla.mla_decode_step_workspace_bytes(c.d, spec.batch, spec.sq)
+    c = H.GpuCase(x, num_splits=num_splits)
+    n = mla.mla_decode_step_workspace_bytes(c.d, spec.batch, spec.sq, num_splits)
     assert n > 0
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     args = (c.d, c.h, c.w_dkv, c.w_kr, c.positions, c.q_nope, c.q_rope, c.w_uk, c.w_uv, c.pool, c.block_table,
             c.seq_lens, x["scale"], ws, c.out)
     if phases_one_by_one:
         for ph in (mla.MLA_PHASE_PREPARE, mla.MLA_PHASE_ATTEND, mla.MLA_PHASE_FINISH):
-            mla.mla_decode_step(*args, lse=c.lse, status=c.status, phases=ph)
+            mla.mla_decode_step(*args, lse=c.lse, status=c.status, phases=ph, num_splits=num_splits)
     else:
-        mla.mla_decode_step(*args, lse=c.lse, status=c.status)
+        mla.mla_decode_step(*args, lse=c.lse, status=c.status, num_splits=num_splits)
     torch.cuda.synchronize()
-    assert int(r.status.item()) == 0 and int(c.status.item()) == 0
+    assert int(r.status.item()) == status and int(c.status.item()) == status
     assert torch.equal(c.pool.view(torch.int16), r.pool.view(torch.int16))
     assert torch.equal(c.out.view(torch.int16), r.out.view(torch.int16))
     assert torch.equal(c.lse, r.lse)
@@ -55,6 +57,32 @@ def test_step_equals_append_then_decode(name, lens, sq, one_by_one):
     ref, lse = H.oracle_decode(x, appended_rows=rows)
     H.assert_close(H.host(c.out), ref, "bf16", name)
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
+def test_step_new_tokens_in_two_ranges():
+    """Two new tokens at positions 127 and 128 of a 129-token sequence, with token ranges of
+    128: the two new rows are read by two ranges, each with two head groups (sq = 2)."""
+    spec = H.small_spec("step_two_ranges", 2, 2, [129, 300], append=True, seed=97)
+    x = synth.make_inputs(spec)
+    H.log("step_two_ranges: new rows 127 | 128 split between ranges")
+    c = _pair(x, num_splits=4)     # 512 rounded tokens: ranges of 128
+    rows = H.oracle_append_rows(x)
+    ref, _ = H.oracle_decode(x, appended_rows=rows)
+    H.assert_close(H.host(c.out), ref, "bf16", "step_two_ranges")
+
+
+def test_step_positions_inside_and_outside_the_context():
+    """Sequence 0 appends at position 100 of 300 (a row inside the context, read by a range
+    that does not hold the context's end), sequence 1 at position -1 (outside every table
+    row: reported, not written, by both paths), sequence 2 at its end."""
+    from mla_rank_latent_amd import mla
+    spec = H.small_spec("step_positions", 3, 1, [300, 200, 150], append=True, seed=98)
+    x = synth.make_inputs(spec)
+    x["positions"] = x["positions"].copy()
+    x["positions"][0, 0] = 100          # ranges of 192 tokens: range 0 of sequence 0
+    x["positions"][1, 0] = -1
+    H.log(f"step_positions: positions {x['positions'][:, 0].tolist()}")
+    _pair(x, num_splits=4, status=mla.MLA_STATUS_BAD_POS)
 
 
 @pytest.mark.timeout(600)
