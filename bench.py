@@ -528,7 +528,7 @@ def main() -> int:
                     help="only run a plain 1 GiB streaming kernel (to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the hot path here runs on a single MI355X and this build has no "
+        print(f"bench.py measures one GPU: the library runs the hot path on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
