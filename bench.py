@@ -51,11 +51,20 @@ COUNTER_PROFILES = {
 }
 
 
+def code_text(text: str) -> str:
+    """C++/HIP source without its comments and with whitespace runs collapsed: what the
+    compiler sees, so that a comment edit does not retire a counter profile."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_sha256(sources) -> str:
+    """sha256 over the code (comments and whitespace aside) of the given source files."""
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode("utf-8"))
     return h.hexdigest()
 
 

@@ -22,7 +22,8 @@
 //           for the wave's own quarter of the 512 latent features and all 128
 //           rows (32 MFMAs).
 // A wave keeps its Q (144 VGPRs) and its O quarter (256 AGPRs) in registers
-// for the whole range.  The softmax weights P of a stage go through LDS
+// for the whole range; Q arrives as 36 contiguous 1 KB runs, the absorbed
+// queries being stored in the MFMA operand order (qlat_byte).  The softmax weights P of a stage go through LDS
 // (8 KB, double-buffered), so every tile operand a wave reads for the latent
 // product feeds four MFMAs (one per row block) and the transposing tile reads
 // drop to a quarter.  The cache tile is read from HBM once per workgroup.
