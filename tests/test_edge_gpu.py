@@ -33,6 +33,8 @@ def _run(spec, num_splits=0, mutate=None):
     (200, 1, [129, 64]),         # two head groups, the second ragged
     (72, 3, [3, 190]),           # 42 heads per group at sq = 3
     (128, 8, [8, 65, 300]),      # the largest query group
+    (64, 1, [100, 257]),         # 64 heads: the absorb tiles' XCD grouping, half-filled rows
+    (192, 2, [5, 130]),          # 192 heads at sq = 2: three head groups, the grouping again
 ])
 def test_head_counts_and_query_groups(n_heads, sq, lens):
     spec = H.small_spec(f"heads{n_heads}_sq{sq}", len(lens), sq, lens, seed=31 + n_heads + sq, n_heads=n_heads)
