@@ -18,7 +18,8 @@
 //    128-byte blocks).  Up to four pieces' loads are in flight per thread and the
 //    piece weights are applied branch-free, so the partial states stream at
 //    memory rate instead of one round trip per piece.  Rows with many pieces (small
-//    batches) split them over several thread slots, combined through LDS.
+//    batches) split them over several thread slots, shared out in proportion to the
+//    rows' piece counts and combined through LDS.
 //  - The merged latent goes to LDS as a bf16 high part and a bf16 remainder
 //    (two MFMAs per step keep the product close to fp32 accuracy).
 //  - Up-projection [32 x 512] . [512 x columns] on MFMA 32x32x16, computed
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
   // space later takes the latent parts' partial products (up to 3 x 32 x 64 fp32)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kMergeRows * kLat * 2 + kMergeRows * kLat * 4];
   __shared__ float s_mx[kMergeRows], s_den[kMergeRows];
+  __shared__ int s_first[kMergeRows / 2], s_nsl[kMergeRows / 2];   // a shared row's first slot and slot count
   MLA_LDS uint8_t* s_hi = (MLA_LDS uint8_t*)smem;
   MLA_LDS uint8_t* s_lo = s_hi + kMergeRows * kLat * 2;
   MLA_LDS uint8_t* s_comb = s_lo + kMergeRows * kLat * 2;
@@ -74,6 +76,23 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
   const int wc = wave % kWc;    // output column block
   const int col0 = ch * kCols + 32 * wc;
 
+  // The rows' piece ranges are loaded first: the memory wait for them then leaves the W^UV
+  // slice below in flight.  Lane k < rv of every wave holds row k's when rows are shared
+  // out (rv <= 16, see the merge), else every slot its own row's.
+  const int rv = M - mb * kMergeRows < kMergeRows ? M - mb * kMergeRows : kMergeRows;
+  const bool shared_rows = rv <= kMergeRows / 2;
+  const int slot = tid >> 4;
+  const int c16 = tid & 15;
+  int i = slot, pl = 0, npl = 1;   // row within the block, piece lane of the row, its slots
+  bool row_ok = slot < rv;
+  int pb0 = 0, pb1 = 0;
+  if (shared_rows ? lane < rv : row_ok) {
+    const int32_t* piece_base = (const int32_t*)(ws + Lw.off_piece);
+    const int bk = (mb * kMergeRows + (shared_rows ? lane : i)) / sq;
+    pb0 = piece_base[bk];
+    pb1 = piece_base[bk + 1];
+  }
+
   // B operand (K = latent, N = output column): lane holds
   // W^UV[128 h + col0 + n][kLat / kParts * kp + 16 ks + 8 hh .. +7], ks = 0 .. kSteps - 1.
   u32x4 bop[kSteps];
@@ -84,21 +103,14 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
   }
 
   // ---- merge.  Sixteen threads (a slot) own one row's 512 columns: thread c16 of a slot
-  // holds columns 64 j + 4 c16 .. +3, j = 0..7.  With rv < 32 valid rows (small batches,
-  // whose sequences are split into many pieces) a row gets pl_n = 32 / rp slots (rp = rv
-  // rounded up to a power of two) that take every pl_n-th piece; their maxima and then
-  // their weighted sums are combined through LDS in slot order.
+  // holds columns 64 j + 4 c16 .. +3, j = 0..7.  With rv <= 16 valid rows (small batches,
+  // whose sequences are split into many pieces) the 32 slots are shared out by piece
+  // count: each row takes one slot, and the other 32 - rv go to the rows in proportion to
+  // their pieces (rounded down), so a long sequence's row, which sets the block's time,
+  // takes the most.  A row's slots are consecutive and take every npl-th piece; their
+  // states are combined through LDS in slot order.
   {
-    const int rv = M - mb * kMergeRows < kMergeRows ? M - mb * kMergeRows : kMergeRows;
-    int rp = 1;
-    while (rp < rv) rp <<= 1;
-    const int pl_n = kMergeRows / rp;
-    const int slot = tid >> 4;
-    const int c16 = tid & 15;
-    const int i = slot % rp;          // row within the block
-    const int pl = slot / rp;         // piece lane of the row
-    const int m = mb * kMergeRows + i;
-    const bool row_ok = i < rv;
+    const int g = h / hg;
     if (rv < kMergeRows) {
       // rows without a slot (or past M) must still hold finite values for the MFMAs
       for (int k = tid; k < kMergeRows * kLat / 4; k += 512) {
@@ -107,6 +119,39 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
       }
       __syncthreads();   // the rows' own values land after the fill
     }
+    int p0 = g * P + pb0, p1 = g * P + pb1;
+    if (shared_rows) {
+      // the shares, from the rows' counts in scalar registers
+      int tot = 0;
+#pragma unroll
+      for (int k = 0; k < kMergeRows / 2; ++k) tot += __builtin_amdgcn_readlane(pb1 - pb0, k);
+      const int ns = 1 + (tot > 0 ? (pb1 - pb0) * (kMergeRows - rv) / tot : 0);   // lane k < rv: row k's slots
+      int start = 0, my_start = 0;
+      row_ok = false;
+      i = 0;   // a slot left over keeps row 0 and no pieces
+#pragma unroll
+      for (int k = 0; k < kMergeRows / 2; ++k) {
+        if (k < rv) {
+          const int nk = __builtin_amdgcn_readlane(ns, k);
+          const int b0k = __builtin_amdgcn_readlane(pb0, k), b1k = __builtin_amdgcn_readlane(pb1, k);
+          if (slot >= start && slot < start + nk) {
+            i = k;
+            pl = slot - start;
+            npl = nk;
+            row_ok = true;
+            p0 = g * P + b0k;
+            p1 = g * P + b1k;
+          }
+          if (lane == k) my_start = start;
+          start += nk;
+        }
+      }
+      if (wave == 0 && lane < rv) {
+        s_first[lane] = my_start;
+        s_nsl[lane] = ns;
+      }
+    }
+    const int m = mb * kMergeRows + i;
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -117,17 +162,13 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     if (row_ok) {
       const int b = m / sq;
       const int s = m - b * sq;
-      const int g = h / hg;
       r = (h - g * hg) * sq + s;
-      const int32_t* piece_base = (const int32_t*)(ws + Lw.off_piece);
-      const int p0 = g * P + piece_base[b];
-      const int p1 = g * P + piece_base[b + 1];
       // online merge: the running maximum rises as pieces arrive and the sums so far are
       // rescaled; up to four pieces' loads (states and weights together) share one round trip
-      for (int p = p0 + pl; p < p1; p += 4 * pl_n) {
+      for (int p = p0 + pl; p < p1; p += 4 * npl) {
         int q[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) q[k] = p + k * pl_n < p1 ? p + k * pl_n : p;   // past the end: weight 0
+        for (int k = 0; k < 4; ++k) q[k] = p + k * npl < p1 ? p + k * npl : p;   // past the end: weight 0
         float2 ml[4];
         u32x2 bv[4][8];
 #pragma unroll
@@ -142,8 +183,9 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
         float mk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) mk[k] = ((k == 0 || q[k] != p) && ml[k].y > 0.0f) ? ml[k].x : -__builtin_inff();
+        // no branch on the weights: the states' loads then issue with the weights' in one
+        // round trip.  Nothing seen yet (mn = -inf) gives sc = 0 and w = 0: the sums stay 0.
         const float mn = fmaxf(fmaxf(Mx, fmaxf(mk[0], mk[1])), fmaxf(mk[2], mk[3]));
-        if (mn == -__builtin_inff()) continue;   // nothing seen yet
         const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - mn);
         float w[4];
 #pragma unroll
@@ -183,39 +225,41 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
         lse[(size_t)mm * n_heads + h] = dn > 0.0f ? (mx + __builtin_amdgcn_logf(dn)) * 0.69314718055994531f
                                                   : -__builtin_inff();
     };
-    if (pl_n == 1) {
+    if (rv > kMergeRows / 2) {
       if (row_ok) {
         if (c16 == 0) put_lse(m, Mx, den);
         put_row(i, c16, acc, den > 0.0f ? 1.0f / den : 0.0f);
       }
     } else {
-      // A row's slots: brought to the row's maximum, their sums combined through LDS in slot
-      // order; every thread then finishes some (row, column-quad) pairs, so the combine's
-      // chain is pl_n reads long for 128 threads per row instead of 31 for 16.
-      if (c16 == 0) s_mx[slot] = Mx;
-      __syncthreads();
-      float Mg = Mx;
-      for (int q = 0; q < pl_n; ++q) Mg = fmaxf(Mg, s_mx[q * rp + i]);
-      const float sc = Mx == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(Mx - Mg);
+      // A row's slots leave their sums, maxima and weight sums in LDS; every thread then
+      // finishes some (row, column-quad) pairs, bringing the row's slots to the row's maximum
+      // and adding them in slot order (npl reads per pair, 128 threads per row).
       MLA_LDS f32x4* comb = (MLA_LDS f32x4*)s_comb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) comb[(slot * 16 + c16) * 8 + j] = acc[j] * sc;
-      if (c16 == 0) s_den[slot] = den * sc;
+      for (int j = 0; j < 8; ++j) comb[(slot * 16 + c16) * 8 + j] = acc[j];
+      if (c16 == 0) {
+        s_mx[slot] = Mx;
+        s_den[slot] = den;
+      }
       __syncthreads();
-      for (int task = tid; task < rp * 128; task += 512) {
-        const int ii = task >> 7, quad = task & 127, jj = quad >> 4, cc = quad & 15;
-        if (ii >= rv) continue;
+      for (int task = tid; task < rv * 128; task += 512) {
+        // a wave's 64 tasks share their row: the slot range and the maxima are uniform
+        const int ii = __builtin_amdgcn_readfirstlane(task >> 7), quad = task & 127, jj = quad >> 4, cc = quad & 15;
+        const int q0 = __builtin_amdgcn_readfirstlane(s_first[ii]);
+        const int q1 = q0 + __builtin_amdgcn_readfirstlane(s_nsl[ii]);
+        float mg = -__builtin_inff();
+#pragma unroll 8
+        for (int q = q0; q < q1; ++q) mg = fmaxf(mg, s_mx[q]);
         f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         float dn = 0.0f;
-        for (int q = 0; q < pl_n; ++q) {
-          sum += comb[((q * rp + ii) * 16 + cc) * 8 + jj];
-          dn += s_den[q * rp + ii];
+#pragma unroll 8
+        for (int q = q0; q < q1; ++q) {
+          const float mq = s_mx[q];
+          const float wq = mq == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mq - mg);   // slot without weight: 0
+          sum += comb[(q * 16 + cc) * 8 + jj] * wq;
+          dn += s_den[q] * wq;
         }
-        if (quad == 0) {
-          float mg = -__builtin_inff();
-          for (int q = 0; q < pl_n; ++q) mg = fmaxf(mg, s_mx[q * rp + ii]);
-          put_lse(mb * kMergeRows + ii, mg, dn);
-        }
+        if (quad == 0) put_lse(mb * kMergeRows + ii, mg, dn);
         const float inv = dn > 0.0f ? 1.0f / dn : 0.0f;
         u32x2 vh, vl;
 #pragma unroll

@@ -71,6 +71,25 @@ def test_every_stage_count_before_the_epilogue(num_splits):
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
 
 
+@pytest.mark.parametrize("name,sq,lens,num_splits", [
+    ("skewed5", 1, [6000, 64, 1500, 130, 3000], 256),    # one row holds most of the pieces
+    ("one_long16", 1, [2000] + [64 + 7 * i for i in range(15)], 256),   # 16 rows: half the slots spare
+    ("second_block8", 1, [70 + 5 * i for i in range(32)] + [4000, 65, 900, 64, 2500, 130, 64, 1200], 512),
+    ("sq2_skewed3", 2, [3000, 66, 700], 128),            # rows of one sequence share its count
+])
+def test_merge_slots_follow_piece_counts(name, sq, lens, num_splits):
+    """A row block with at most 16 valid rows shares its 32 thread slots out by the rows'
+    piece counts: lengths far apart put many pieces on one row and one or two on the
+    others, and a block of 8 rows after a full block of 32; every head of every row is
+    compared with the oracle."""
+    spec = H.small_spec(name, len(lens), sq, lens, seed=53 + len(lens))
+    x, c = _run(spec, num_splits=num_splits)
+    assert int(c.status.item()) == 0
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", spec.name)
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
 def test_more_splits_than_work():
     """1024 ranges for 3 short sequences: most ranges are empty."""
     spec = H.small_spec("splits1024", 3, 1, [1, 65, 130], seed=43)
