@@ -135,8 +135,9 @@ __global__ __launch_bounds__(256) void append_partial_bf16_kernel(const uint16_t
                                                                   const uint16_t* __restrict__ w_kr, int tokens,
                                                                   int d_model, int nslice, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[prep::kAppendPartialLds];
-  prep::append_partial_tile(h, w_dkv, w_kr, tokens, d_model, nslice, part, (MLA_LDS uint8_t*)smem, blockIdx.x,
-                            blockIdx.y, blockIdx.z);
+  int ct, tg, sl;
+  prep::append_tile_of(blockIdx.x, kRow / 32, (tokens + 63) / 64, nslice, &ct, &tg, &sl);
+  prep::append_partial_tile(h, w_dkv, w_kr, tokens, d_model, nslice, part, (MLA_LDS uint8_t*)smem, ct, tg, sl);
 }
 
 __global__ __launch_bounds__(256) void append_finish_bf16_kernel(const float* __restrict__ part, int nslice,
@@ -352,7 +353,7 @@ hipError_t launch_append_split_bf16(const uint16_t* h, const uint16_t* w_dkv, co
                                     uint16_t* cache, int num_blocks, int tokens, int t_per_seq, int d_model,
                                     float rope_base, float* ws, int32_t* status, hipStream_t st) {
   const int nslice = append_split_slices(d_model);
-  dim3 grid1(kRow / 32, (tokens + 63) / 64, nslice);
+  dim3 grid1((kRow / 32) * ((tokens + 63) / 64) * nslice);
   hipLaunchKernelGGL(append_partial_bf16_kernel, grid1, dim3(256), 0, st, h, w_dkv, w_kr, tokens, d_model, nslice,
                      ws);
   hipError_t e = hipGetLastError();

@@ -84,6 +84,19 @@ __device__ __forceinline__ void append_partial_tile(const uint16_t* __restrict__
     }
 }
 
+// Tile of the split append for linear index a = 0 .. T - 1, T = n_ct * n_tg * nslice.  The
+// n_ct column tiles of one (token group, slice) read the same 64 x 32 k-step block of h,
+// so they should share an XCD (and its L2): block ids equal modulo 8 share one, and with
+// T a multiple of 8 the ids a with a % 8 = r take the r-th eighth of the tiles in
+// (slice, token group, column tile) order.  Otherwise a is that order itself.
+__device__ __forceinline__ void append_tile_of(int a, int n_ct, int n_tg, int nslice, int* ct, int* tg, int* sl) {
+  const int T = n_ct * n_tg * nslice;
+  const int s = T % 8 == 0 ? (a % 8) * (T / 8) + a / 8 : a;
+  *ct = s % n_ct;
+  *tg = (s / n_ct) % n_tg;
+  *sl = s / (n_ct * n_tg);
+}
+
 // ---- absorbed queries
 constexpr int kAbsorbLds = kNope * 256;   // the 128 x 128 W^UK slice
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }

@@ -29,10 +29,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     return;
   }
   if (bid <= n_app) {
-    const int a = bid - 1;
-    const int n_ct = kRow / 32, n_tg = (tokens + 63) / 64;
-    prep::append_partial_tile(h, w_dkv, w_kr, tokens, d_model, nslice, part, (MLA_LDS uint8_t*)smem, a % n_ct,
-                              (a / n_ct) % n_tg, a / (n_ct * n_tg));
+    int ct, tg, sl;
+    prep::append_tile_of(bid - 1, kRow / 32, (tokens + 63) / 64, nslice, &ct, &tg, &sl);
+    prep::append_partial_tile(h, w_dkv, w_kr, tokens, d_model, nslice, part, (MLA_LDS uint8_t*)smem, ct, tg, sl);
     return;
   }
   prep::absorb_tile(q_nope, q_rope, w_uk, batch, sq, n_heads, qscale, ws, Lw, (MLA_LDS uint8_t*)smem,
