@@ -5,8 +5,9 @@ lse must be equal bit for bit (the same kernels' code computes them), and the ou
 match the oracle.  Covers one and two new tokens per sequence, ragged paged batches,
 the phases called one by one, two new tokens that fall in two token ranges, new
 positions inside the context rather than at its end and outside every table row
-(reported, not written), the batch-64 context-8192 benchmark step, and a step of 2048
-new tokens (mla_cache_append's many-row GEMM path)."""
+(reported, not written), model widths with 7, 8 and 23 append slices, the batch-64
+context-8192 benchmark step, and a step of 2048 new tokens (mla_cache_append's many-row
+GEMM path)."""
 import numpy as np
 import pytest
 
@@ -57,6 +58,28 @@ def test_step_equals_append_then_decode(name, lens, sq, one_by_one):
     ref, lse = H.oracle_decode(x, appended_rows=rows)
     H.assert_close(H.host(c.out), ref, "bf16", name)
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
+@pytest.mark.parametrize("d_model", [2048, 2560, 7168])
+def test_step_other_model_widths(d_model):
+    """Model widths whose append splits d_model into 7, 8 and 23 slices: with 18 column
+    tiles per 64-token group, 8 slices give a tile count that is a multiple of 8 (tiles
+    that read one block of h grouped per XCD), 7 and 23 do not (tiles in plain slice
+    order); both paths write the same rows as mla_cache_append and match the oracle."""
+    spec = H.small_spec(f"step_dmodel{d_model}", 3, 1, [130, 64, 300], append=True, seed=99, d_model=d_model)
+    x = synth.make_inputs(spec)
+    H.log(f"step d_model={d_model}")
+    c = _pair(x)
+    rows = H.oracle_append_rows(x)
+    ref, lse = H.oracle_decode(x, appended_rows=rows)
+    H.assert_close(H.host(c.out), ref, "bf16", spec.name)
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+    pool = H.host(c.pool)
+    for b in range(3):
+        p = int(x["positions"][b, 0])
+        g = pool[x["block_table"][b, p // 64], p % 64]
+        # every element of the written row within one bf16 ulp of the oracle's rounded row
+        assert np.all(np.abs(g - rows[b, 0]) <= H.bf16_ulp(rows[b, 0]) + 1e-30)
 
 
 def test_step_new_tokens_in_two_ranges():
