@@ -105,6 +105,7 @@ bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L
   }
   if (W > (1 << 20)) return false;
   L->W = W;
+  L->tune = num_splits <= 0 ? 1 : 0;
   L->P = W + batch;
   const size_t R = (size_t)d->d_latent + d->d_rope;
   size_t off = 0;

@@ -108,6 +108,43 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
   // 64-token blocks, so that small batches do not write (and merge) more partial-state bytes
   // than the cache bytes they read.
   if (align == kBlk && quota < kMinRangeTokens) quota = kMinRangeTokens;
+  // A range that holds a sequence boundary runs a second piece, which costs about
+  // kPieceCostTokens of attention work, and the slowest range sets the kernel's time.  When
+  // the range count is the library's choice, quotas q0, q0 + align, ... (fewer ranges) are
+  // weighed by q + kPieceCostTokens * (most boundaries inside one range), and the cheapest is
+  // taken (the first on ties): batch 4 with 128K/64K/32K/16K contexts, for one, gets 240
+  // ranges of 1024 tokens that each hold one sequence's tokens only, not 256 ranges of 960
+  // of which three hold two sequences.  Boundaries at seg[1 .. batch-1] (multiples of align).
+  if (Lw.tune && batch > 1 && num_wg <= kPlanBins) {
+    __shared__ int s_bins[kPlanBins];
+    __shared__ int s_most;
+    int best_q = quota, best_cost = 0x7fffffff;
+    for (int c = 0; c < kQuotaTries; ++c) {
+      const int q = quota + c * align;
+      const int nr = (total + q - 1) / q;   // ranges at this quota (<= num_wg)
+      for (int i = t; i < nr; i += 256) s_bins[i] = 0;
+      if (t == 0) s_most = 0;
+      __syncthreads();
+      for (int b = t; b < batch; b += 256) {
+        const int s0 = batch <= 256 ? my_s0 : seg[b];   // thread b kept its segment start
+        if (b > 0 && s0 < total && s0 % q != 0) atomicAdd(&s_bins[s0 / q], 1);
+      }
+      __syncthreads();
+      int most = 0;
+      for (int i = t; i < nr; i += 256) most = s_bins[i] > most ? s_bins[i] : most;
+      if (most > 0) atomicMax(&s_most, most);
+      __syncthreads();
+      const int cost = q + kPieceCostTokens * s_most;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best_q = q;
+      }
+      const bool done = s_most == 0;   // no boundary inside a range: larger quotas cost more
+      __syncthreads();                 // s_bins and s_most are reset by the next try
+      if (done) break;
+    }
+    quota = best_q;
+  }
   __syncthreads();
   // pass 2: pieces per sequence = number of ranges its segment meets
   if (t == 0) s_carry = 0;

@@ -25,6 +25,12 @@ constexpr int kStageBytes = kSubTok * kRow * 2;        // 36864
 constexpr int kChunksPerRow = kRow * 2 / 16;           // 72 chunks of 16 B
 constexpr int kMaxSqBf16 = 8;
 constexpr int kMinRangeTokens = 2 * kBlk;   // smallest token range of the bf16 split plan
+// What a range pays for each sequence boundary inside it (a second piece: another query
+// load, another partial state written, the copy pipeline refilled), in cached tokens'
+// worth of attention work: 14.9 us measured at 960-token ranges and ~1.9 GHz, ~234 tokens.
+constexpr int kPieceCostTokens = 4 * kBlk;
+constexpr int kQuotaTries = 8;              // quotas the planner weighs (q0, q0 + align, ...)
+constexpr int kPlanBins = 512;              // most ranges the planner weighs them for
 // FP8 latent cache page (MLA_DTYPE_BF16_FP8): 64 rows of E4M3 codes, then 64 bf16
 // k^R rows, then 64 fp32 scales
 constexpr int kFp8RopeOff = kBlk * kLat;                       // 32768
@@ -54,8 +60,8 @@ constexpr int kF32MaxSq = 64;
 
 // ---------------------------------------------------------------------------
 // Split plan.  The per-group token space is the concatenation over sequences
-// of seq_len rounded up to `align`; it is cut into `num_wg` equal ranges of
-// `quota` tokens.  Every (range, sequence) intersection is one piece with its
+// of seq_len rounded up to `align`; it is cut into equal ranges of `quota` tokens,
+// at most `num_wg` of them.  Every (range, sequence) intersection is one piece with its
 // own partial softmax state.  Written on the device by plan_build().
 // ---------------------------------------------------------------------------
 struct PlanHeader {
@@ -73,6 +79,7 @@ struct WsLayout {
   int W;              // ranges (workgroups) per head group
   int P;              // max pieces per head group = W + batch
   int align;          // token alignment of ranges
+  int tune;           // the range count was left to the library: the planner may use fewer
   size_t off_hdr, off_seg, off_piece, off_wgseg, off_qlat, off_lse, off_o, total;
 };
 

@@ -90,6 +90,29 @@ def test_merge_slots_follow_piece_counts(name, sq, lens, num_splits):
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
 
 
+def test_planner_keeps_sequences_out_of_shared_ranges():
+    """With the range count left to the library, the planner weighs a few range lengths by
+    the extra pieces that ranges holding a sequence boundary cost.  Lengths 20480, 10240,
+    5120 and 3200 on 256 ranges would cut ranges of 192 tokens, two of which hold a
+    boundary; ranges of 256 tokens hold one sequence each, so the plan (the workspace's
+    header: total tokens, tokens per range, pieces) has as many pieces as ranges.  Every
+    head of every sequence is compared with the oracle."""
+    import torch
+    lens = [20480, 10240, 5120, 3200]
+    spec = H.small_spec("planner_aligned", len(lens), 1, lens, seed=59)
+    x, c = _run(spec)
+    assert int(c.status.item()) == 0
+    total, quota, pieces = (int(v) for v in c.ws[:12].view(torch.int32).cpu())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    q0 = max(128, -(-(-(-total // cus)) // 64) * 64)
+    H.log(f"  plan: total {total}, quota {quota} (even split {q0}), pieces {pieces}")
+    assert total == sum(lens) and quota % 64 == 0 and q0 <= quota <= q0 + 7 * 64
+    assert pieces == -(-total // quota)   # no range holds two sequences
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", spec.name)
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
 def test_more_splits_than_work():
     """1024 ranges for 3 short sequences: most ranges are empty."""
     spec = H.small_spec("splits1024", 3, 1, [1, 65, 130], seed=43)
