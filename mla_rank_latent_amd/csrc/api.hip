@@ -113,6 +113,8 @@ bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L
   L->off_seg = off;   off += up((size_t)(batch + 1) * 4);
   L->off_piece = off; off += up((size_t)(batch + 1) * 4);
   L->off_wgseg = off; off += up((size_t)W * 4);
+  L->off_rcut = off;  off += up((size_t)(W + 1) * 4);
+  L->off_firstr = off; off += up((size_t)batch * 4);
   const size_t qrows = (size_t)batch * sq * d->n_heads;
   L->off_qlat = off;  off += up((bf ? qlat_padded_rows(qrows) : qrows) * R * elem_size(d->dtype));
   L->off_lse = off;   off += up((size_t)L->G * L->P * L->rows * 8);

@@ -132,7 +132,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
   }
   if (w >= W) return;
 
-  const MLA_CONST PlanHeader* hdr = as_const((const PlanHeader*)(ws + Lw.off_hdr));
   const MLA_CONST int32_t* seg = as_const((const int32_t*)(ws + Lw.off_seg));
   const MLA_CONST int32_t* piece_base = as_const((const int32_t*)(ws + Lw.off_piece));
   const MLA_CONST int32_t* wgseg = as_const((const int32_t*)(ws + Lw.off_wgseg));
@@ -142,11 +141,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
   float2* part_ml = (float2*)(ws + Lw.off_lse);
   uint16_t* part_o = (uint16_t*)(ws + Lw.off_o);   // bf16
 
-  const int total = hdr->total;
-  const int quota = hdr->quota;
-  const int lo = w * quota;
-  if (lo >= total) return;
-  const int hi = lo + quota < total ? lo + quota : total;
+  // this range's tokens [lo, hi) of the concatenated sequences (empty past the plan's ranges)
+  const MLA_CONST int32_t* rcut = as_const((const int32_t*)(ws + Lw.off_rcut));
+  const MLA_CONST int32_t* firstr = as_const((const int32_t*)(ws + Lw.off_firstr));
+  const int lo = rcut[w];
+  const int hi = rcut[w + 1];
+  if (lo >= hi) return;
 
   // this lane's query row inside the head group
   const int row = wave * kRowsPerWave + n;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fp8_kernel(
       continue;
     }
     const int b = seg_i;
-    const int piece = g * P + piece_base[b] + (w - s0 / quota);
+    const int piece = g * P + piece_base[b] + (w - firstr[b]);
     int L = lens[b];
     {
       const int cap = max_blocks * kBlk;

@@ -46,10 +46,11 @@ __host__ __device__ constexpr int waitcnt_vm(int n) {
 }
 
 // ---------------------------------------------------------------------------
-// Split planner: one 256-thread workgroup writes the plan for `batch`
-// sequences into the workspace.  seg_start[b] = sum over b' < b of
-// roundup(clamped len, align); piece_base[b] = number of pieces before
-// sequence b; wg_seg[w] = the sequence holding token w * quota.
+// Split planner: one 256-thread workgroup writes the plan for `batch` sequences into the
+// workspace.  seg_start[b] = sum over b' < b of roundup(clamped len, align); the token
+// space [0, total) is cut into at most num_wg ranges, range w = [rcut[w], rcut[w + 1]);
+// piece_base[b] = number of pieces before sequence b; first_range[b] = the range holding
+// sequence b's first token; wg_seg[w] = the sequence holding range w's first token.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_len(int L, int sq, int max_blocks, int bsz, int32_t* status) {
   int cap = max_blocks * bsz;
@@ -60,17 +61,42 @@ __device__ __forceinline__ int clamp_len(int L, int sq, int max_blocks, int bsz,
   return L;
 }
 
+// number of v[0 .. n) below x (lower bound) / at most x (upper bound); v nondecreasing
+__device__ __forceinline__ int count_below(const int* v, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ int count_upto(const int* v, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v[mid] <= x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_blocks, int bsz, int align,
                            int num_wg, uint8_t* ws, const WsLayout& Lw, int32_t* status) {
   __shared__ int s_scan[256];
   __shared__ int s_carry;
+  __shared__ int s_cut[kPlanBins];   // range starts of a cost-balanced plan; the quota search's bins
+  __shared__ int s_most;
   PlanHeader* hdr = (PlanHeader*)(ws + Lw.off_hdr);
   int32_t* seg = (int32_t*)(ws + Lw.off_seg);
   int32_t* piece = (int32_t*)(ws + Lw.off_piece);
   int32_t* wgseg = (int32_t*)(ws + Lw.off_wgseg);
+  int32_t* rcut = (int32_t*)(ws + Lw.off_rcut);
+  int32_t* firstr = (int32_t*)(ws + Lw.off_firstr);
   const int t = threadIdx.x;
   // pass 1: prefix sums of rounded lengths -> seg_start, and the total.  With at most 256
-  // sequences each thread keeps its segment for pass 2 instead of reading it back.
+  // sequences each thread keeps its segment for pass 2 instead of reading it back, and
+  // s_scan[b - 1] keeps boundary b (the start of sequence b) until pass 2.
   int my_s0 = 0, my_s1 = 0;
   if (t == 0) s_carry = 0;
   __syncthreads();
@@ -107,31 +133,41 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
   // tokens (1152 B each) would cost to read: ranges of the bf16 kernels take at least two
   // 64-token blocks, so that small batches do not write (and merge) more partial-state bytes
   // than the cache bytes they read.
-  if (align == kBlk && quota < kMinRangeTokens) quota = kMinRangeTokens;
+  const int min_range = align == kBlk ? kMinRangeTokens : align;
+  if (quota < min_range) quota = min_range;
   // A range that holds a sequence boundary runs a second piece, which costs about
   // kPieceCostTokens of attention work, and the slowest range sets the kernel's time.  When
-  // the range count is the library's choice, quotas q0, q0 + align, ... (fewer ranges) are
-  // weighed by q + kPieceCostTokens * (most boundaries inside one range), and the cheapest is
-  // taken (the first on ties): batch 4 with 128K/64K/32K/16K contexts, for one, gets 240
-  // ranges of 1024 tokens that each hold one sequence's tokens only, not 256 ranges of 960
-  // of which three hold two sequences.  Boundaries at seg[1 .. batch-1] (multiples of align).
+  // the range count is the library's choice, two plans are weighed by that cost of their
+  // slowest range (tokens + kPieceCostTokens per boundary inside), and the cheaper is kept
+  // (the even one on ties):
+  //  - even ranges of q tokens, q = q0, q0 + align, ... (fewer ranges): the cost is
+  //    q + kPieceCostTokens * (most boundaries inside one range).  Batch 4 with
+  //    128K/64K/32K/16K contexts gets 240 ranges of 1024 tokens that each hold one
+  //    sequence's tokens, not 256 ranges of 960 of which three hold two sequences;
+  //  - (up to 256 sequences) cost-balanced ranges: with C(x) = x + kPieceCostTokens *
+  //    (boundaries below token x), range w starts where C reaches w / W of its total, at the
+  //    next multiple of align, or at the boundary itself when that is at most one align
+  //    step back or the cost target falls inside a boundary's step.  Ragged batches, whose
+  //    even ranges hold several boundaries each, get ranges that are shorter where they
+  //    hold boundaries.
+  // Boundaries are seg[1 .. batch-1] below total (multiples of align).
+  bool balanced = false;
+  int nwb = 0;   // ranges of the balanced plan
   if (Lw.tune && batch > 1 && num_wg <= kPlanBins) {
-    __shared__ int s_bins[kPlanBins];
-    __shared__ int s_most;
     int best_q = quota, best_cost = 0x7fffffff;
     for (int c = 0; c < kQuotaTries; ++c) {
       const int q = quota + c * align;
       const int nr = (total + q - 1) / q;   // ranges at this quota (<= num_wg)
-      for (int i = t; i < nr; i += 256) s_bins[i] = 0;
+      for (int i = t; i < nr; i += 256) s_cut[i] = 0;
       if (t == 0) s_most = 0;
       __syncthreads();
       for (int b = t; b < batch; b += 256) {
         const int s0 = batch <= 256 ? my_s0 : seg[b];   // thread b kept its segment start
-        if (b > 0 && s0 < total && s0 % q != 0) atomicAdd(&s_bins[s0 / q], 1);
+        if (b > 0 && s0 < total && s0 % q != 0) atomicAdd(&s_cut[s0 / q], 1);
       }
       __syncthreads();
       int most = 0;
-      for (int i = t; i < nr; i += 256) most = s_bins[i] > most ? s_bins[i] : most;
+      for (int i = t; i < nr; i += 256) most = s_cut[i] > most ? s_cut[i] : most;
       if (most > 0) atomicMax(&s_most, most);
       __syncthreads();
       const int cost = q + kPieceCostTokens * s_most;
@@ -140,22 +176,79 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
         best_q = q;
       }
       const bool done = s_most == 0;   // no boundary inside a range: larger quotas cost more
-      __syncthreads();                 // s_bins and s_most are reset by the next try
+      __syncthreads();                 // s_cut and s_most are reset by the next try
       if (done) break;
     }
     quota = best_q;
+    if (batch <= 256 && best_cost > quota) {
+      // boundaries s_scan[0 .. nb) (sequence b + 1 starts at s_scan[b])
+      const int nb = count_below(s_scan, batch - 1, total);
+      const long long ctot = (long long)total + (long long)kPieceCostTokens * nb;
+      long long wl = ctot / min_range;
+      wl = wl < 1 ? 1 : wl;
+      const int wb = wl < num_wg ? (int)wl : num_wg;
+      for (int w = t; w < wb; w += 256) {
+        int cut = 0;
+        if (w > 0) {
+          const long long y = (long long)w * ctot / wb;
+          // k = boundaries whose step C has fully passed below y
+          int lo = 0, hi = nb;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((long long)s_scan[mid] + (long long)kPieceCostTokens * (mid + 1) < y) lo = mid + 1;
+            else hi = mid;
+          }
+          const int sk = lo > 0 ? s_scan[lo - 1] : 0;
+          const int sk1 = lo < nb ? s_scan[lo] : total;
+          const long long x = y - (long long)kPieceCostTokens * lo;
+          long long tc = (x + align - 1) / align * align;
+          if (tc > sk1) tc = sk1;
+          cut = lo > 0 && (int)tc - sk <= align ? sk : (int)tc;   // sk: a boundary when lo > 0
+        }
+        s_cut[w] = cut;
+      }
+      if (t == 0) s_most = 0;
+      __syncthreads();
+      for (int w = t; w < wb; w += 256) {
+        const int lo = s_cut[w], hi = w + 1 < wb ? s_cut[w + 1] : total;
+        if (hi > lo) {
+          const int inside = count_below(s_scan, nb, hi) - count_upto(s_scan, nb, lo);
+          atomicMax(&s_most, hi - lo + kPieceCostTokens * inside);
+        }
+      }
+      __syncthreads();
+      balanced = s_most < best_cost;
+      nwb = wb;
+    }
   }
   __syncthreads();
+  // the plan's ranges: their count, where range w starts, and the range holding token x
+  // (balanced is uniform: each branch reads the LDS cuts only on the plan that has them)
+  const int nw = balanced ? nwb : (total + quota - 1) / quota;
+  auto cut_of = [&](int w) {
+    if (w >= nw) return total;
+    if (balanced) return s_cut[w];
+    return w * quota;
+  };
+  auto range_of = [&](int x) {
+    if (balanced) return count_upto(s_cut, nw, x) - 1;
+    return x / quota;
+  };
+  for (int w = t; w <= num_wg; w += 256) rcut[w] = cut_of(w);
   // pass 2: pieces per sequence = number of ranges its segment meets
   if (t == 0) s_carry = 0;
   __syncthreads();
   for (int base = 0; base < batch; base += 256) {
     int b = base + t;
-    int v = 0, s0 = 0, s1 = 0;
+    int v = 0, s0 = 0, s1 = 0, r0 = 0, r1 = -1;
     if (b < batch) {
       s0 = batch <= 256 ? my_s0 : seg[b];
       s1 = batch <= 256 ? my_s1 : seg[b + 1];
-      v = s1 > s0 ? (s1 - 1) / quota - s0 / quota + 1 : 0;
+      if (s1 > s0) {
+        r0 = range_of(s0);
+        r1 = range_of(s1 - 1);
+        v = r1 - r0 + 1;
+      }
     }
     s_scan[t] = v;
     __syncthreads();
@@ -167,9 +260,10 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
     }
     if (b < batch) {
       piece[b] = s_carry + s_scan[t] - v;
+      firstr[b] = r0;
       // ranges whose first token falls in this segment start their walk here
       if (s1 > s0) {
-        for (int w = (s0 + quota - 1) / quota; w * quota < s1 && w < num_wg; ++w) wgseg[w] = b;
+        for (int w = cut_of(r0) < s0 ? r0 + 1 : r0; w <= r1; ++w) wgseg[w] = b;
       }
     }
     __syncthreads();
@@ -179,7 +273,7 @@ __device__ void plan_build(const int32_t* seq_lens, int batch, int sq, int max_b
   if (t == 0) {
     piece[batch] = s_carry;
     hdr->total = total;
-    hdr->quota = quota;
+    hdr->quota = balanced ? 0 : quota;
     hdr->pieces = s_carry;
     hdr->status = 0;
   }

@@ -192,24 +192,23 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(mla_dims d, const float* 
   const int r = blockIdx.y;   // row = head * sq + s
   const int H = d.n_heads, R = d.d_latent + d.d_rope, dc = d.d_latent, bs = d.block_size;
   const int head = r / sq, s = r % sq;
-  const PlanHeader* hdr = (const PlanHeader*)(ws + Lw.off_hdr);
   const int32_t* seg = (const int32_t*)(ws + Lw.off_seg);
   const int32_t* piece_base = (const int32_t*)(ws + Lw.off_piece);
   const int32_t* wgseg = (const int32_t*)(ws + Lw.off_wgseg);
   const float* q_lat = (const float*)(ws + Lw.off_qlat);
   float* part_o = (float*)(ws + Lw.off_o);
   float2* part_ml = (float2*)(ws + Lw.off_lse);
-  const int total = hdr->total, quota = hdr->quota;
-  const int lo = w * quota;
-  if (lo >= total) return;
-  const int hi = min(lo + quota, total);
+  const int32_t* rcut = (const int32_t*)(ws + Lw.off_rcut);
+  const int32_t* firstr = (const int32_t*)(ws + Lw.off_firstr);
+  const int lo = rcut[w], hi = rcut[w + 1];   // this range's tokens (empty past the plan's ranges)
+  if (lo >= hi) return;
   constexpr int kPer = kF32MaxWidth / 256;   // latent columns per thread
   for (int b = wgseg[w]; b < batch; ++b) {
     const int s0 = seg[b], s1 = seg[b + 1];
     if (s0 >= hi) break;
     const int a = max(lo, s0) - s0, e = min(hi, s1) - s0;
     if (a >= e) continue;
-    const int piece = piece_base[b] + (w - s0 / quota);
+    const int piece = piece_base[b] + (w - firstr[b]);
     const int L = min(max(seq_lens[b], 0), max_blocks * bs);
     const int lim = L - sq + s;   // last visible token
     const int tend = min(e, lim + 1);

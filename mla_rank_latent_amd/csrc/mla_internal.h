@@ -60,13 +60,14 @@ constexpr int kF32MaxSq = 64;
 
 // ---------------------------------------------------------------------------
 // Split plan.  The per-group token space is the concatenation over sequences
-// of seq_len rounded up to `align`; it is cut into equal ranges of `quota` tokens,
-// at most `num_wg` of them.  Every (range, sequence) intersection is one piece with its
-// own partial softmax state.  Written on the device by plan_build().
+// of seq_len rounded up to `align`; it is cut into at most `num_wg` ranges (equal ones of
+// `quota` tokens, or cost-balanced ones, quota 0), range w = [rcut[w], rcut[w + 1]).  Every
+// (range, sequence) intersection is one piece with its own partial softmax state.  Written
+// on the device by plan_build().
 // ---------------------------------------------------------------------------
 struct PlanHeader {
   int32_t total;      // tokens in the (rounded) space of one head group
-  int32_t quota;      // tokens per range (multiple of align)
+  int32_t quota;      // tokens per range (multiple of align); 0 for cost-balanced ranges
   int32_t pieces;     // pieces per head group
   int32_t status;     // reserved
 };
@@ -80,7 +81,7 @@ struct WsLayout {
   int P;              // max pieces per head group = W + batch
   int align;          // token alignment of ranges
   int tune;           // the range count was left to the library: the planner may use fewer
-  size_t off_hdr, off_seg, off_piece, off_wgseg, off_qlat, off_lse, off_o, total;
+  size_t off_hdr, off_seg, off_piece, off_wgseg, off_rcut, off_firstr, off_qlat, off_lse, off_o, total;
 };
 
 bool ws_layout(const mla_dims* d, int batch, int sq, int num_splits, WsLayout* L);

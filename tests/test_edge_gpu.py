@@ -113,6 +113,32 @@ def test_planner_keeps_sequences_out_of_shared_ranges():
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
 
 
+@pytest.mark.parametrize("name,sq,lens", [
+    ("ragged24_sq1", 1, [5132, 4555, 9064, 9286, 5703, 8086, 8933, 8538, 2163, 5261, 9917, 11967, 8511, 11977, 3584,
+                         11378, 10241, 2388, 2190, 8256, 9248, 8050, 6976, 7295]),
+    ("ragged40_sq2", 2, [1833, 1732, 528, 1977, 2971, 739, 2166, 1411, 938, 261, 269, 2522, 2804, 88, 2005, 96, 2107,
+                         2811, 2295, 2911, 748, 2580, 295, 2080, 2156, 497, 2860, 2725, 904, 1529, 424, 2110, 1047,
+                         99, 2576, 379, 1073, 2094, 1266, 2847]),
+])
+def test_planner_balances_ragged_batches(name, sq, lens):
+    """Ragged batches whose even ranges would hold several sequence boundaries each get
+    cost-balanced ranges (the plan header's quota 0): ranges are shorter where they hold
+    boundaries.  The pieces stay within the workspace's bound, and every head of every
+    sequence (and query token) matches the oracle."""
+    import torch
+    spec = H.small_spec(name, len(lens), sq, lens, seed=61 + sq)
+    x, c = _run(spec)
+    assert int(c.status.item()) == 0
+    total, quota, pieces = (int(v) for v in c.ws[:12].view(torch.int32).cpu())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H.log(f"  plan: total {total}, quota {quota}, pieces {pieces}")
+    assert total == sum(-(-v // 64) * 64 for v in lens)
+    assert quota == 0 and len(lens) <= pieces <= cus // (1 if sq == 1 else 2) + len(lens)
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", spec.name)
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
 def test_more_splits_than_work():
     """1024 ranges for 3 short sequences: most ranges are empty."""
     spec = H.small_spec("splits1024", 3, 1, [1, 65, 130], seed=43)
