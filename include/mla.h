@@ -228,7 +228,11 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s
  * block_table[batch, max_blocks]            int32 (device)
  * seq_lens   [batch]                        int32 (device), query tokens included
  * softmax_scale  e.g. 1/sqrt(d_nope + d_rope)
- * num_splits 0 = one attention workgroup per compute unit; >0 forces the count
+ * num_splits 0 = at most one attention workgroup per compute unit, the token ranges
+ *            chosen by the library (even ranges, or for ragged batches of up to
+ *            256 sequences ranges that are shorter where they hold a sequence
+ *            boundary, whichever makes the slowest range cheaper); >0 forces the
+ *            count, with even ranges
  * workspace  device scratch of at least mla_decode_workspace_bytes(dims, batch,
  *            sq, num_splits) bytes, 256-byte aligned; its contents on entry do
  *            not matter and are clobbered
