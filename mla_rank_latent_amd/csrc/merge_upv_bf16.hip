@@ -22,6 +22,9 @@
 //    rows' piece counts and combined through LDS.
 //  - The merged latent goes to LDS as a bf16 high part and a bf16 remainder
 //    (two MFMAs per step keep the product close to fp32 accuracy).
+//  - A block with one query row (batch 1 at one query token) takes the row in fp32 and
+//    multiplies it with the W^UV slice on the vector units (each output column a product of
+//    512, split over 4 or 8 adjacent threads); otherwise:
 //  - Up-projection [32 x 512] . [512 x columns] on MFMA 32x32x16, computed
 //    transposed so that each lane ends with four adjacent output columns per
 //    register group (8-byte stores): each wave takes 32 output columns over one
@@ -93,10 +96,21 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     pb1 = piece_base[bk + 1];
   }
 
-  // B operand (K = latent, N = output column): lane holds
+  // The workgroup's W^UV slice, loaded before the merge starts.  Several rows: the B operand
+  // of the MFMA up-projection (K = latent, N = output column), lane holding
   // W^UV[128 h + col0 + n][kLat / kParts * kp + 16 ks + 8 hh .. +7], ks = 0 .. kSteps - 1.
+  // One row (rv = 1: batch 1 at one query token): a product of the row with the slice, thread
+  // t holding latent elements 8 (t % kTpc + kTpc ks) .. +7, ks = 0 .. kSteps - 1, of output
+  // column t / kTpc of the workgroup's kCols (the kTpc threads of a column read whole 128-byte
+  // runs of its row at each step).
+  constexpr int kTpc = 512 / kCols;   // threads per output column on the one-row path
+  static_assert(kTpc * 8 * kSteps == kLat, "one-row slice covers the latent");
   u32x4 bop[kSteps];
-  {
+  if (rv == 1) {
+    const uint16_t* wp = w_uv + ((size_t)h * kNope + ch * kCols + tid / kTpc) * kLat + (tid % kTpc) * 8;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) bop[ks] = *(const u32x4*)(wp + 8 * kTpc * ks);
+  } else {
     const uint16_t* wp = w_uv + ((size_t)h * kNope + col0 + n) * kLat + (kLat / kParts) * kp + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) bop[ks] = *(const u32x4*)(wp + 16 * ks);
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
   // states are combined through LDS in slot order.
   {
     const int g = h / hg;
-    if (rv < kMergeRows) {
+    if (rv > 1 && rv < kMergeRows) {
       // rows without a slot (or past M) must still hold finite values for the MFMAs
       for (int k = tid; k < kMergeRows * kLat / 4; k += 512) {
         ((MLA_LDS u32x2*)s_hi)[k] = u32x2{0u, 0u};
@@ -261,6 +275,10 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
         }
         if (quad == 0) put_lse(mb * kMergeRows + ii, mg, dn);
         const float inv = dn > 0.0f ? 1.0f / dn : 0.0f;
+        if (rv == 1) {   // the one row, fp32, for the one-row product: columns 64 jj + 4 cc .. +3
+          *(MLA_LDS f32x4*)((MLA_LDS float*)s_hi + 64 * jj + 4 * cc) = sum * inv;
+          continue;
+        }
         u32x2 vh, vl;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -276,6 +294,27 @@ __global__ __launch_bounds__(512) void merge_upv_bf16_kernel(const uint16_t* __r
     }
   }
   __syncthreads();
+
+  if (rv == 1) {
+    // ---- one row: out[column] = W^UV row . o_lat in fp32, the kTpc partial sums of a column
+    // (adjacent lanes) added by a butterfly in a fixed order
+    const MLA_LDS float* ol = (const MLA_LDS float*)s_hi + (tid % kTpc) * 8;
+    float a = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const f32x4 o0 = *(const MLA_LDS f32x4*)(ol + 8 * kTpc * ks);
+      const f32x4 o1 = *(const MLA_LDS f32x4*)(ol + 8 * kTpc * ks + 4);
+      const u32x4 wv = bop[ks];
+      a += bf2f((uint16_t)(wv[0] & 0xffffu)) * o0[0] + bf2f((uint16_t)(wv[0] >> 16)) * o0[1] +
+           bf2f((uint16_t)(wv[1] & 0xffffu)) * o0[2] + bf2f((uint16_t)(wv[1] >> 16)) * o0[3] +
+           bf2f((uint16_t)(wv[2] & 0xffffu)) * o1[0] + bf2f((uint16_t)(wv[2] >> 16)) * o1[1] +
+           bf2f((uint16_t)(wv[3] & 0xffffu)) * o1[2] + bf2f((uint16_t)(wv[3] >> 16)) * o1[3];
+    }
+#pragma unroll
+    for (int off = kTpc / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+    if (tid % kTpc == 0) out[((size_t)(mb * kMergeRows) * n_heads + h) * kNope + ch * kCols + tid / kTpc] = f2bf(a);
+    return;
+  }
 
   // ---- out[32 rows x 32 cols of this wave] over latent part kp
   f32x16 acc;

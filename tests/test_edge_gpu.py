@@ -139,6 +139,23 @@ def test_planner_balances_ragged_batches(name, sq, lens):
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
 
 
+@pytest.mark.parametrize("name,lens,num_splits", [
+    ("one_row_300", [300], 0),
+    ("one_row_5000_s7", [5000], 7),
+    ("rows33", [100 + 37 * i for i in range(33)], 0),   # the second block of 32 rows holds one
+])
+def test_blocks_of_one_row(name, lens, num_splits):
+    """A merge row block that holds a single query row (batch 1 at one query token, or the
+    33rd row) multiplies it with the W^UV slice on the vector units instead of the
+    32-row MFMA product; with one and several pieces, compared with the oracle."""
+    spec = H.small_spec(name, len(lens), 1, lens, seed=67 + len(lens))
+    x, c = _run(spec, num_splits=num_splits)
+    assert int(c.status.item()) == 0
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", spec.name)
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
 def test_more_splits_than_work():
     """1024 ranges for 3 short sequences: most ranges are empty."""
     spec = H.small_spec("splits1024", 3, 1, [1, 65, 130], seed=43)
