@@ -119,6 +119,11 @@ def test_planner_keeps_sequences_out_of_shared_ranges():
     ("ragged40_sq2", 2, [1833, 1732, 528, 1977, 2971, 739, 2166, 1411, 938, 261, 269, 2522, 2804, 88, 2005, 96, 2107,
                          2811, 2295, 2911, 748, 2580, 295, 2080, 2156, 497, 2860, 2725, 904, 1529, 424, 2110, 1047,
                          99, 2576, 379, 1073, 2094, 1266, 2847]),
+    # short batches whose cost targets step less than one boundary's piece cost: several
+    # targets fall inside one boundary's step, so the plan has empty ranges at boundaries,
+    # which no sequence may count as a piece
+    ("tiny5_sq2", 2, [34, 131, 137, 188, 3]),
+    ("tiny6_sq1", 1, [192, 7, 182, 62, 168, 90]),
 ])
 def test_planner_balances_ragged_batches(name, sq, lens):
     """Ragged batches whose even ranges would hold several sequence boundaries each get
