@@ -346,6 +346,8 @@ int mla_decode_step(const mla_dims* dims, const mla_step_args* args, int32_t pha
  *    MLA_NOALLOC_SCRATCH_BYTES returns MLA_ERR_SCRATCH_TOO_SMALL before anything is
  *    launched (64 MiB holds batch 64 x 128 heads at one query token, the decode
  *    benchmark's shape, with room to spare; use mla_decode for larger shapes).
+ *  - The GPU is the calling thread's current device (hipGetDevice): the stream must
+ *    belong to it, as for any launch of that device's kernels.
  *  - Every call on one GPU uses that GPU's one array, and nothing in it has to start
  *    at any value (each call writes what it reads).  Calls that overlap in time on
  *    one GPU (other streams, other host threads) race on it and give wrong results:
