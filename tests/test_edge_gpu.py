@@ -144,6 +144,26 @@ def test_planner_balances_ragged_batches(name, sq, lens):
     assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
 
 
+@pytest.mark.parametrize("name,batch,sq,num_splits", [
+    ("b300_sq1", 300, 1, 0),      # two 256-sequence chunks in the planner's scans
+    ("b520_sq1", 520, 1, 0),      # three chunks; 17 row blocks of 32 in the absorb and the merge
+    ("b300_sq2", 300, 2, 0),      # two head groups, 600 query rows per head
+    ("b300_sq1_s64", 300, 1, 64),  # a forced range count: ranges holding many sequence boundaries
+])
+def test_batches_beyond_256_sequences(name, batch, sq, num_splits):
+    """More than 256 sequences: the split planner's prefix sums run over several 256-sequence
+    chunks and read the segment starts back from the workspace (no cost-balanced plan), and
+    the absorb and merge kernels see more than eight 32-row blocks.  Every sequence, query
+    token and head is compared with the oracle."""
+    lens = [sq + (37 * b + 11) % 250 for b in range(batch)]
+    spec = H.small_spec(name, batch, sq, lens, seed=71 + batch + sq)
+    x, c = _run(spec, num_splits)
+    assert int(c.status.item()) == 0
+    ref, lse = H.oracle_decode(x)
+    H.assert_close(H.host(c.out), ref, "bf16", spec.name)
+    assert np.max(np.abs(H.host(c.lse) - lse)) <= 2e-2
+
+
 @pytest.mark.parametrize("name,lens,num_splits", [
     ("one_row_300", [300], 0),
     ("one_row_5000_s7", [5000], 7),

@@ -48,6 +48,8 @@ def _pair(x, phases_one_by_one=False, num_splits=0, status=0):
     ("step_b3_sq1", [130, 64, 700], 1, False),
     ("step_b4_sq2", [2, 65, 513, 1000], 2, False),
     ("step_b3_phases", [200, 77, 1500], 1, True),
+    # 300 sequences: five 64-token append groups, the planner's scans over two chunks
+    ("step_b300_sq1", [1 + (41 * b + 5) % 300 for b in range(300)], 1, False),
 ])
 def test_step_equals_append_then_decode(name, lens, sq, one_by_one):
     spec = H.small_spec(name, len(lens), sq, lens, append=True, seed=91 + sq)
