@@ -100,3 +100,16 @@ def test_fp8_full_size_whole_output():
     ref, lse = H.oracle_decode(x, appended_rows=app)
     assert not np.isnan(ref).any()
     _check(c, ref, lse, "fp8 v2_b64_ctx8192_paged_append whole output")
+
+
+def test_one_sequence_of_a_million_tokens():
+    """One sequence of 2^20 cached tokens (an eighth of the 2^23 tokens a table row may
+    address), paged over 16384 permuted blocks: 256 token ranges of 4096 tokens each, the
+    largest token and block offsets any test reaches.  Three heads (the first, one in the
+    middle, the last) against the oracle."""
+    spec = synth.Spec("v2_b1_ctx1m", batch=1, sq=1, seed=7, seq_lens=[1 << 20], paged=True)
+    x = synth.make_inputs(spec)
+    c = _run(x)
+    ref, lse = H.oracle_decode(x, heads=[0, 77, 127])
+    assert int(np.count_nonzero(~np.isnan(lse))) == 3
+    _check(c, ref, lse, "v2_b1_ctx1m heads 0, 77, 127")
