@@ -98,6 +98,8 @@ def _fp8_case(spec, num_splits=0):
     ("fp8_h16_b3", 3, 1, [64, 130, 900], True, 16),
     ("fp8_h72_b2_sq2", 2, 2, [33, 2000], True, 72),
     ("fp8_h200_b2", 2, 1, [97, 640], True, 200),
+    # 300 sequences: the planner's scans over two 256-sequence chunks, ten row blocks of 32
+    ("fp8_paged_b300", 300, 1, [1 + (37 * b + 11) % 250 for b in range(300)], True, 128),
 ])
 def test_fp8_decode_matches_oracle(name, batch, sq, lens, paged, n_heads):
     spec = synth.Spec(name, batch=batch, sq=sq, seq_lens=list(lens), paged=paged, seed=43 + batch + sq,
