@@ -35,6 +35,9 @@ def _run(spec, num_splits=0, mutate=None):
     (128, 8, [8, 65, 300]),      # the largest query group
     (64, 1, [100, 257]),         # 64 heads: the absorb tiles' XCD grouping, half-filled rows
     (192, 2, [5, 130]),          # 192 heads at sq = 2: three head groups, the grouping again
+    (1, 1, [50, 300]),           # one head: 127 of a workgroup's 128 rows are padding
+    (8, 2, [2, 700]),            # 8 heads at two query tokens
+    (1024, 1, [130, 64]),        # the most heads the kernels take: eight head groups
 ])
 def test_head_counts_and_query_groups(n_heads, sq, lens):
     spec = H.small_spec(f"heads{n_heads}_sq{sq}", len(lens), sq, lens, seed=31 + n_heads + sq, n_heads=n_heads)
