@@ -18,7 +18,9 @@
  *  - Array pointers are DEVICE pointers owned by the caller (unless a comment
  *    says host).  The library never allocates, frees or synchronises; every
  *    launch is asynchronous on the caller's stream (`stream` is a hipStream_t,
- *    NULL = the default stream).
+ *    NULL = the default stream).  Kernel launches are the only stream work
+ *    (no memset or copy), so a stream under HIP graph capture records them as
+ *    they are, and a replay with the same buffers repeats the call.
  *  - Arrays are dense, row-major, in the element type named by dims->dtype
  *    (MLA_DTYPE_F32: float, MLA_DTYPE_BF16 and MLA_DTYPE_BF16_FP8: bfloat16)
  *    unless typed int32/float; with MLA_DTYPE_BF16_FP8 the cache alone is in
