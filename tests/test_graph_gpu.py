@@ -88,3 +88,31 @@ def test_decode_replays_from_a_graph():
     c = H.GpuCase(x)
     g = _capture(c.decode)
     _check_replays(g, c, ref, None)
+
+
+def test_decode_graph_follows_new_lengths_and_queries():
+    """A serving loop captures once and replays with new contents in the same buffers: the plan
+    is rebuilt on the device from seq_lens at every replay, so shorter lengths and other queries
+    give what an eager call on those contents gives."""
+    import torch
+    lens, new_lens = [1000, 3, 257], [500, 2, 64]
+    spec = H.small_spec("graph_contents", len(lens), 2, lens, seed=173)
+    x = synth.make_inputs(spec)
+    H.log(f"graph decode lens={lens} -> {new_lens} sq=2")
+    c = H.GpuCase(x)
+    g = _capture(c.decode)
+    ref = H.GpuCase(x)
+    for case in (c, ref):
+        case.seq_lens.copy_(torch.tensor(new_lens, dtype=torch.int32))
+        case.q_nope.neg_()
+        case.q_rope.mul_(0.5)
+    ref.decode()
+    torch.cuda.synchronize()
+    assert int(ref.status.item()) == 0
+    c.out.zero_()
+    c.lse.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert int(c.status.item()) == 0
+    assert torch.equal(c.out.view(torch.int16), ref.out.view(torch.int16))
+    assert torch.equal(c.lse, ref.lse)
