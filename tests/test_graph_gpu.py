@@ -5,7 +5,9 @@ the eager call's cache, out and lse bit for bit.  Before each replay the outputs
 the appended rows are taken out of the cache again and other work runs on the device, so a
 replay that skipped a kernel, or read state left by the previous one, would show.  Covers
 mla_decode_step (the append's partial products, the absorbed queries and the plan, the
-append's rows, the attention, the merge) and mla_decode alone."""
+append's rows, the attention, the merge), mla_decode alone (also replayed with new lengths
+and queries in the same buffers), the FP8-cache decode, and prefill run in groups of
+sequences."""
 import pytest
 
 from mla_rank_latent_amd import synth
@@ -116,3 +118,39 @@ def test_decode_graph_follows_new_lengths_and_queries():
     assert int(c.status.item()) == 0
     assert torch.equal(c.out.view(torch.int16), ref.out.view(torch.int16))
     assert torch.equal(c.lse, ref.lse)
+
+
+def test_fp8_decode_replays_from_a_graph():
+    """The FP8-cache decode (pages made by mla_cache_quantize) captured and replayed."""
+    import torch
+    lens = [700, 1, 130]
+    spec = H.small_spec("graph_fp8", len(lens), 1, lens, seed=174)
+    x = H.with_fp8_cache(synth.make_inputs(spec))
+    H.log(f"graph fp8 decode lens={lens}")
+    ref = H.GpuCase(x, cache="fp8")
+    ref.decode()
+    torch.cuda.synchronize()
+    assert int(ref.status.item()) == 0
+    c = H.GpuCase(x, cache="fp8")
+    g = _capture(c.decode)
+    _check_replays(g, c, ref, None)
+
+
+def test_prefill_in_groups_replays_from_a_graph():
+    """mla_prefill with a workspace for two of five sequences (expand, then attend, per group,
+    all on the capture stream) captured and replayed."""
+    import torch
+    from mla_rank_latent_amd import mla
+    spec = synth.Spec("graph_prefill", batch=5, sq=96, seq_lens=[700, 300, 1000, 129, 512], paged=True, seed=175,
+                      n_heads=16)
+    x = synth.make_inputs(spec)
+    H.log("graph prefill, 5 sequences in groups of 2")
+    ref = H.PrefillCase(x)
+    ref.run()
+    torch.cuda.synchronize()
+    assert int(ref.status.item()) == 0
+    c = H.PrefillCase(x)
+    per_seq = mla.mla_prefill_workspace_bytes(c.d, 1, int(x["block_table"].shape[1]))
+    c.ws = torch.empty(2 * per_seq, dtype=torch.uint8, device="cuda")
+    g = _capture(c.run)
+    _check_replays(g, c, ref, None)
