@@ -6,8 +6,8 @@ the appended rows are taken out of the cache again and other work runs on the de
 replay that skipped a kernel, or read state left by the previous one, would show.  Covers
 mla_decode_step (the append's partial products, the absorbed queries and the plan, the
 append's rows, the attention, the merge), mla_decode alone (also replayed with new lengths
-and queries in the same buffers), the FP8-cache decode, and prefill run in groups of
-sequences."""
+and queries in the same buffers), the FP8-cache decode, the decode that allocates nothing,
+and prefill run in groups of sequences."""
 import pytest
 
 from mla_rank_latent_amd import synth
@@ -153,4 +153,24 @@ def test_prefill_in_groups_replays_from_a_graph():
     per_seq = mla.mla_prefill_workspace_bytes(c.d, 1, int(x["block_table"].shape[1]))
     c.ws = torch.empty(2 * per_seq, dtype=torch.uint8, device="cuda")
     g = _capture(c.run)
+    _check_replays(g, c, ref, None)
+
+
+def test_noalloc_decode_replays_from_a_graph():
+    """mla_decode_noalloc, the entry point for callers that cannot allocate (code under graph
+    capture among them), captured and replayed: each replay equals mla_decode with a caller
+    workspace, bit for bit."""
+    import torch
+    from mla_rank_latent_amd import mla
+    lens = [900, 5, 320, 64]
+    spec = H.small_spec("graph_noalloc", len(lens), 1, lens, seed=176)
+    x = synth.make_inputs(spec)
+    H.log(f"graph noalloc decode lens={lens}")
+    ref = H.GpuCase(x)
+    ref.decode()
+    torch.cuda.synchronize()
+    assert int(ref.status.item()) == 0
+    c = H.GpuCase(x)
+    g = _capture(lambda: mla.mla_decode_noalloc(c.d, c.q_nope, c.q_rope, c.w_uk, c.w_uv, c.pool, c.block_table,
+                                                c.seq_lens, x["scale"], c.out, lse=c.lse, status=c.status))
     _check_replays(g, c, ref, None)
