@@ -354,6 +354,9 @@ int mla_decode_step(const mla_dims* dims, const mla_step_args* args, int32_t pha
  *    at any value (each call writes what it reads).  Calls that overlap in time on
  *    one GPU (other streams, other host threads) race on it and give wrong results:
  *    order them on one stream, or use mla_decode with separate workspaces.
+ *  - Under HIP graph capture: make one call on the device before capturing, so the
+ *    address lookup is not part of the captured region; a replay then runs in the
+ *    same array, and replays overlapping other calls on that GPU race like calls do.
  */
 #define MLA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 int mla_decode_noalloc(const mla_dims* dims, const void* q_nope, const void* q_rope,
